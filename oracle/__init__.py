@@ -1,0 +1,131 @@
+"""Plain fp64 CPU oracle for C = A @ B -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. It shares no code with the HIP library and never imports
+it. The arithmetic lives in `ref_gemm.c` (plain C, fp64, k-ascending sums);
+`brute.py` is an exact rational cross-check for tiny shapes.
+
+Dtype codes here are the oracle's own: "f32", "f16", "bf16".
+
+Parity status: every function is pinned (tests/test_oracle.py) against the
+pages' worked examples, closed forms, invariants and an exact brute force.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build
+
+_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        lib = ctypes.CDLL(LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.ref_threads.restype = ctypes.c_int
+        lib.ref_decode.argtypes = [ctypes.c_int, p, i64, p]
+        lib.ref_encode.argtypes = [ctypes.c_int, p, i64, p]
+        lib.ref_gemm.argtypes = [i64, i64, i64, ctypes.c_int, p, i64, i64, p, i64, i64, p, i64]
+        lib.ref_gemm.restype = ctypes.c_int
+        lib.ref_gemm_entries.argtypes = [i64, ctypes.c_int, p, i64, i64, p, i64, i64, i64, p, p, p]
+        lib.ref_gemm_rows.argtypes = [i64, i64, i64, i64, ctypes.c_int, p, i64, i64, p, i64, i64, p]
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return _load().ref_threads()
+
+
+def _bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    want = _BITS[dtype]
+    if x.dtype != want:
+        raise TypeError(f"oracle expects raw {dtype} bits as {np.dtype(want).name}, got {x.dtype}")
+    return x
+
+
+def _operand(x: np.ndarray, dtype: str):
+    """Base pointer and element strides of a (possibly strided) bit array view."""
+    x = _bits(x, dtype)
+    item = x.itemsize
+    if any(s % item for s in x.strides) or any(s < 0 for s in x.strides):
+        raise ValueError("oracle operands need non-negative, element-aligned strides")
+    return x.ctypes.data, tuple(s // item for s in x.strides)
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of each element of a bit-pattern array."""
+    b = np.ascontiguousarray(_bits(bits, dtype))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().ref_decode(_CODES[dtype], b.ctypes.data, b.size, out.ctypes.data)
+    return out
+
+
+def encode(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values to `dtype`, nearest with ties to even; returns bits."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=_BITS[dtype])
+    _load().ref_encode(_CODES[dtype], v.ctypes.data, v.size, out.ctypes.data)
+    return out
+
+
+def gemm(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str) -> np.ndarray:
+    """C = A @ B in fp64 (k-ascending sums over exactly decoded inputs).
+
+    a_bits: [M, K] view of raw bits; b_bits: [K, N] view; any non-negative
+    strides (a transposed view is read through its strides).
+    """
+    (M, K), (K2, N) = a_bits.shape, b_bits.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    pa, (sam, sak) = _operand(a_bits, dtype)
+    pb, (sbk, sbn) = _operand(b_bits, dtype)
+    c = np.zeros((M, N), dtype=np.float64)
+    rc = _load().ref_gemm(M, N, K, _CODES[dtype], pa, sam, sak, pb, sbk, sbn, c.ctypes.data, N)
+    if rc != 0:
+        raise MemoryError("oracle could not allocate its fp64 operand copies")
+    return c
+
+
+def gemm_entries(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str,
+                 rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """C[rows[t], cols[t]] for each t, each straight from the definition."""
+    (M, K), (K2, N) = a_bits.shape, b_bits.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols must have the same shape")
+    if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+        raise IndexError("sampled index outside C")
+    pa, (sam, sak) = _operand(a_bits, dtype)
+    pb, (sbk, sbn) = _operand(b_bits, dtype)
+    out = np.empty(rows.shape, dtype=np.float64)
+    _load().ref_gemm_entries(K, _CODES[dtype], pa, sam, sak, pb, sbk, sbn,
+                             rows.size, rows.ctypes.data, cols.ctypes.data, out.ctypes.data)
+    return out
+
+
+def gemm_rows(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str,
+              row0: int, nrows: int) -> np.ndarray:
+    """Rows [row0, row0+nrows) of C, each entry straight from the definition."""
+    (M, K), (K2, N) = a_bits.shape, b_bits.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if row0 < 0 or nrows < 0 or row0 + nrows > M:
+        raise IndexError("row range outside C")
+    pa, (sam, sak) = _operand(a_bits, dtype)
+    pb, (sbk, sbn) = _operand(b_bits, dtype)
+    out = np.empty((nrows, N), dtype=np.float64)
+    _load().ref_gemm_rows(row0, nrows, N, K, _CODES[dtype], pa, sam, sak, pb, sbk, sbn,
+                          out.ctypes.data)
+    return out

@@ -1,0 +1,47 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def load_golden(name):
+    """Parse a fixture: blocks of `LABEL rows cols` followed by rows of numbers."""
+    blocks = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.lstrip().startswith("#")]
+    i = 0
+    while i < len(lines):
+        label, r, c = lines[i].split()
+        r, c = int(r), int(c)
+        rows = [[int(x) for x in lines[i + 1 + t].split()] for t in range(r)]
+        assert all(len(row) == c for row in rows), (name, label)
+        blocks[label] = rows
+        i += 1 + r
+    return blocks
+
+
+def load_grid_counts():
+    out = []
+    with open(os.path.join(GOLDEN, "grid_counts.txt")) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln and not ln.startswith("#"):
+                out.append([int(x) for x in ln.split()])
+    return out
+
+
+@pytest.fixture(scope="session")
+def oracle_mod():
+    import oracle
+    oracle.build()
+    return oracle
