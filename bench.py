@@ -1,0 +1,159 @@
+"""Benchmark: TFLOP/s and fraction of the MFMA dense peak of C = A @ B on one MI355X.
+
+One step is one product over the workload's synthetic operands (seeded, see
+dense_gemm_07_amd/inputs.py), inputs already resident in HBM. The config is
+autotuned once before timing (a one-time cost, reported separately); the timed
+steps call the library's normal gemm entry point, which uses the cached
+winner. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense: MFMA bf16/fp16, fp32
+HBM_GBPS = 8000.0
+METRIC = "TFLOP/s and % of MFMA dense peak, 4096³ bf16 GEMM on 1 MI355X"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["dense_gemm_07_amd/csrc/dg_kernels.hpp", "dense_gemm_07_amd/csrc/dg_internal.hpp",
+                  "dense_gemm_07_amd/csrc/mfma_inst.inc"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, a_cpu, b_cpu, target_s=10.0):
+    """The oracle, as it stands, on a row slice of the same product."""
+    import oracle
+    from dense_gemm_07_amd import inputs
+
+    oracle.build()
+    A = inputs.bits(a_cpu, w.in_dtype)
+    B = inputs.bits(b_cpu, w.in_dtype)
+    # Two probes separate the fixed cost (decoding B) from the per-row cost,
+    # then the slice is sized to about target_s of wall time (at most all of C).
+    probes = []
+    for r in (min(w.M, 16), min(w.M, 64)):
+        t0 = time.perf_counter()
+        oracle.gemm(A[:r], B, w.in_dtype)
+        probes.append((r, time.perf_counter() - t0))
+    (r1, t1), (r2, t2) = probes
+    per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-9)
+    rows = int(min(w.M, max(r2, (target_s - max(t1 - per_row * r1, 0.0)) / per_row)))
+    rows -= rows % 8 if rows > 8 else 0
+    if rows > r2:
+        t0 = time.perf_counter()
+        oracle.gemm(A[:rows], B, w.in_dtype)
+        dt = time.perf_counter() - t0
+    else:
+        rows, dt = r2, t2
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of C (A[{rows},{w.K}] @ B[{w.K},{w.N}], {w.in_dtype}), "
+                      f"{dt:.2f} s wall, fp64 k-ascending sums"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square_4096_bf16")
+    ap.add_argument("--no-autotune", action="store_true", help="time the heuristic config instead")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the product shards without exchange, but no multi-GPU path is built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dense_gemm_07_amd as dg
+    from dense_gemm_07_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a_cpu, b_cpu = inputs.make(w, seed=0)
+    a = inputs.to_device_like(a_cpu, dev)
+    b = inputs.to_device_like(b_cpu, dev)
+    c = torch.empty((w.M, w.N), dtype=inputs.TORCH_DTYPES[w.out_dtype], device=dev)
+    torch.cuda.synchronize()
+
+    tune_s = 0.0
+    if not args.no_autotune:
+        t0 = time.perf_counter()
+        cfg, _ = dg.autotune(a, b, out=c, repeats=10)
+        tune_s = time.perf_counter() - t0
+    cfg, _ = dg.select_config(a, b, c)
+    print(f"# workload {w.name}: config {cfg} (autotune {tune_s:.2f} s)", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        dg.gemm(a, b, out=c, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        dg.gemm(a, b, out=c, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.in_dtype]
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic",
+        "config": {"workload": f"gemm {w.M}x{w.N}x{w.K} {w.in_dtype}->{w.out_dtype}",
+                   "name": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "b_layout": "col-major" if w.b_colmajor else "row-major",
+                   "kernel_config": cfg.as_dict(), "autotune_s": round(tune_s, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, a_cpu, b_cpu)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,616 @@
+// Host side of the dense GEMM library: argument validation, the kernel
+// registry, config selection (cache, then heuristic), the autotuner and the
+// config cache. Every public symbol is declared in include/dg.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cinttypes>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "dg.h"
+#include "dg_internal.hpp"
+
+namespace dg {
+namespace {
+
+thread_local std::string g_last_error;
+
+dg_status fail(dg_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char *v = getenv("DG_LOG");
+        return v && *v && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+int elem_size(int dt) { return dt == DG_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == DG_F32 || dt == DG_F16 || dt == DG_BF16; }
+const char *dtype_name(int dt) { return dt == DG_F32 ? "f32" : dt == DG_F16 ? "f16" : dt == DG_BF16 ? "bf16" : "?"; }
+
+struct Problem {
+    int64_t M, N, K;
+    const void *A, *B;
+    const void *C;
+    int64_t sam, sak, sbk, sbn, scm, scn;
+    int in, out;
+};
+
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// A 2D strided view with extents e1, e2 >= 2 and strides s1, s2 >= 1 maps two
+// distinct index pairs to one element iff di*s1 == dj*s2 has a solution with
+// |di| < e1, |dj| < e2, (di, dj) != 0. The smallest one is di = s2/g,
+// dj = s1/g with g = gcd(s1, s2).
+bool injective_2d(int64_t e1, int64_t s1, int64_t e2, int64_t s2) {
+    if (e1 <= 1 || e2 <= 1) return true;
+    const int64_t g = gcd64(s1, s2);
+    return !(s2 / g < e1 && s1 / g < e2);
+}
+
+dg_status validate(const Problem &p) {
+    if (!dtype_ok(p.in)) return fail(DG_ERR_INVALID_VALUE, "unknown input dtype %d", p.in);
+    if (!dtype_ok(p.out)) return fail(DG_ERR_INVALID_VALUE, "unknown output dtype %d", p.out);
+    if (p.M < 0 || p.N < 0 || p.K < 0)
+        return fail(DG_ERR_INVALID_VALUE, "negative dimension (M=%" PRId64 ", N=%" PRId64 ", K=%" PRId64 ")", p.M, p.N, p.K);
+    const int64_t lim = (int64_t)1 << 30;
+    if (p.M > lim || p.N > lim || p.K > lim)
+        return fail(DG_ERR_UNSUPPORTED, "dimension above 2^30 (M=%" PRId64 ", N=%" PRId64 ", K=%" PRId64 ")", p.M, p.N, p.K);
+    if (p.sam < 0 || p.sak < 0 || p.sbk < 0 || p.sbn < 0)
+        return fail(DG_ERR_INVALID_VALUE, "negative A/B stride");
+    const bool c_used = p.M > 0 && p.N > 0;
+    if (c_used && (p.scm < 1 || p.scn < 1)) return fail(DG_ERR_INVALID_VALUE, "C strides must be >= 1");
+    if (c_used && !injective_2d(p.M, p.scm, p.N, p.scn))
+        return fail(DG_ERR_INVALID_VALUE, "C strides (%" PRId64 ", %" PRId64 ") make elements of C overlap", p.scm, p.scn);
+    if (p.M > 0 && p.K > 0 && !p.A) return fail(DG_ERR_INVALID_VALUE, "A is NULL");
+    if (p.K > 0 && p.N > 0 && !p.B) return fail(DG_ERR_INVALID_VALUE, "B is NULL");
+    if (c_used && !p.C) return fail(DG_ERR_INVALID_VALUE, "C is NULL");
+    const uintptr_t ie = (uintptr_t)elem_size(p.in), oe = (uintptr_t)elem_size(p.out);
+    if (((uintptr_t)p.A % ie) || ((uintptr_t)p.B % ie))
+        return fail(DG_ERR_INVALID_VALUE, "A or B not aligned to its element size");
+    if ((uintptr_t)p.C % oe) return fail(DG_ERR_INVALID_VALUE, "C not aligned to its element size");
+    return DG_OK;
+}
+
+// ---- layout classes --------------------------------------------------------
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Load mode of an operand viewed as rows x K with strides (srow, sk), for the
+// 16-bit MFMA kernels (8 elements = 16 bytes per vector).
+int load_mode(const void *base, int64_t rows, int64_t K, int64_t srow, int64_t sk) {
+    if (!aligned16(base)) return LD_GN;
+    const bool row_ok = rows <= 1 || srow % 8 == 0;
+    const bool k_ok = K <= 1 || sk % 8 == 0;
+    if (sk == 1 && row_ok) return LD_KC;
+    if (srow == 1 && k_ok) return LD_RC;
+    return LD_GN;
+}
+
+int c_class(const Problem &p) { return p.scn == 1 ? 0 : p.scm == 1 ? 1 : 2; }
+
+// ---- registry ----------------------------------------------------------------
+
+const std::vector<KernelEntry> &registry() {
+    static const std::vector<KernelEntry> reg = [] {
+        std::vector<KernelEntry> r;
+        register_simt(r);
+        register_mfma_bf16(r);
+        register_mfma_f16(r);
+        return r;
+    }();
+    return reg;
+}
+
+bool same_kernel(const dg_config &a, const dg_config &b) {
+    return a.block_m == b.block_m && a.block_n == b.block_n && a.block_k == b.block_k && a.waves == b.waves &&
+           a.stages == b.stages && a.variant == b.variant;
+}
+
+// Effective load modes of the MFMA kernels for a problem: the four vector
+// combinations are compiled; anything with an element-load operand uses the
+// element-load kernel for both.
+std::pair<int, int> mfma_modes(const Problem &p) {
+    int la = load_mode(p.A, p.M, p.K, p.sam, p.sak);
+    int lb = load_mode(p.B, p.N, p.K, p.sbn, p.sbk);
+    if (la == LD_GN || lb == LD_GN) la = lb = LD_GN;
+    return {la, lb};
+}
+
+const KernelEntry *find_kernel(const dg_config &cfg, const Problem &p) {
+    int la = -1, lb = -1;
+    if (cfg.variant == DG_VARIANT_MFMA) std::tie(la, lb) = mfma_modes(p);
+    for (const auto &e : registry()) {
+        if (!same_kernel(e.cfg, cfg)) continue;
+        if (e.in_dtype != p.in) continue;
+        if (e.out_dtype != -1 && e.out_dtype != p.out) continue;
+        if (e.load_a != -1 && e.load_a != la) continue;
+        if (e.load_b != -1 && e.load_b != lb) continue;
+        return &e;
+    }
+    return nullptr;
+}
+
+// Distinct kernel shapes (one per tile config) usable for a dtype pair.
+std::vector<dg_config> kernel_shapes(int in, int out) {
+    std::vector<dg_config> shapes;
+    for (const auto &e : registry()) {
+        if (e.in_dtype != in || (e.out_dtype != -1 && e.out_dtype != out)) continue;
+        if (in != DG_F32 && e.cfg.variant == DG_VARIANT_SIMT) continue;  // matrix cores for 16-bit inputs
+        bool seen = false;
+        for (const auto &s : shapes) seen = seen || same_kernel(s, e.cfg);
+        if (!seen) shapes.push_back(e.cfg);
+    }
+    return shapes;
+}
+
+const int kGroups[] = {1, 4, 8, 16};
+
+std::vector<dg_config> candidates(int in, int out) {
+    std::vector<dg_config> c;
+    for (const auto &s : kernel_shapes(in, out))
+        for (int xcd = 1; xcd >= 0; --xcd)
+            for (int g : kGroups) {
+                dg_config x = s;
+                x.group_m = g;
+                x.xcd_remap = xcd;
+                c.push_back(x);
+            }
+    return c;
+}
+
+// ---- device facts ------------------------------------------------------------
+
+struct DeviceInfo {
+    int cus = 256;
+    int num_xcd = 8;
+};
+
+std::mutex g_dev_mu;
+std::map<int, DeviceInfo> g_dev;
+
+DeviceInfo device_info() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return DeviceInfo{};
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto it = g_dev.find(dev);
+    if (it != g_dev.end()) return it->second;
+    DeviceInfo d;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+        d.cus = cus;
+        d.num_xcd = std::max(1, cus / 32);  // CDNA4: 32 CUs per XCD
+    } else {
+        (void)hipGetLastError();
+    }
+    g_dev[dev] = d;
+    return d;
+}
+
+// ---- heuristic ---------------------------------------------------------------
+
+dg_config heuristic(const Problem &p, int cus) {
+    const auto shapes = kernel_shapes(p.in, p.out);
+    dg_config best{};
+    bool have = false;
+    if (p.in == DG_F32) {
+        // fp32 inputs: the scalar kernel, the small tile for tiny problems.
+        for (const auto &s : shapes) {
+            const bool small = p.M * p.N <= 64 * 64 * 16;
+            if ((small && s.block_m == 32) || (!small && s.block_m == 64)) {
+                best = s;
+                have = true;
+            }
+        }
+    } else {
+        // Largest tile that still gives at least one tile per CU; else the
+        // smallest tile. Shapes are registered largest first.
+        for (const auto &s : shapes) {
+            const int64_t tiles = ((p.M + s.block_m - 1) / s.block_m) * ((p.N + s.block_n - 1) / s.block_n);
+            if (tiles >= cus) {
+                best = s;
+                have = true;
+                break;
+            }
+        }
+        if (!have && !shapes.empty()) {
+            best = shapes.back();
+            have = true;
+        }
+    }
+    if (!have && !shapes.empty()) best = shapes.front();
+    best.group_m = 8;
+    best.xcd_remap = 1;
+    return best;
+}
+
+// ---- cache -------------------------------------------------------------------
+
+struct Key {
+    int64_t M, N, K;
+    int in, out, la, lb, lc;
+    bool operator<(const Key &o) const {
+        return std::tie(M, N, K, in, out, la, lb, lc) < std::tie(o.M, o.N, o.K, o.in, o.out, o.la, o.lb, o.lc);
+    }
+};
+
+std::mutex g_cache_mu;
+std::map<Key, dg_config> g_cache;
+
+Key key_of(const Problem &p) {
+    Key k{p.M, p.N, p.K, p.in, p.out, -1, -1, c_class(p)};
+    if (p.in != DG_F32) std::tie(k.la, k.lb) = mfma_modes(p);
+    return k;
+}
+
+bool cache_get(const Key &k, dg_config &out) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    auto it = g_cache.find(k);
+    if (it == g_cache.end()) return false;
+    out = it->second;
+    return true;
+}
+
+void cache_put(const Key &k, const dg_config &c) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache[k] = c;
+}
+
+// ---- launch ------------------------------------------------------------------
+
+dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream) {
+    if (p.M == 0 || p.N == 0) return DG_OK;
+    if (cfg.block_m <= 0 || cfg.block_n <= 0 || cfg.block_k <= 0)
+        return fail(DG_ERR_NO_CONFIG, "config has non-positive block sizes");
+    if (cfg.group_m < 1) return fail(DG_ERR_NO_CONFIG, "config group_m must be >= 1");
+    const KernelEntry *e = find_kernel(cfg, p);
+    if (!e)
+        return fail(DG_ERR_NO_CONFIG,
+                    "no compiled kernel for block %dx%dx%d waves %d stages %d variant %d with %s -> %s inputs",
+                    cfg.block_m, cfg.block_n, cfg.block_k, cfg.waves, cfg.stages, cfg.variant, dtype_name(p.in),
+                    dtype_name(p.out));
+    const int64_t gm = (p.M + cfg.block_m - 1) / cfg.block_m;
+    const int64_t gn = (p.N + cfg.block_n - 1) / cfg.block_n;
+    const int64_t threads = (int64_t)cfg.waves * 64;
+    if (gm * gn * threads >= ((int64_t)1 << 32) || gm * gn >= ((int64_t)1 << 31))
+        return fail(DG_ERR_UNSUPPORTED, "too many tiles (%" PRId64 " x %" PRId64 ")", gm, gn);
+    GemmArgs g{};
+    g.A = p.A;
+    g.B = p.B;
+    g.C = const_cast<void *>(p.C);
+    g.M = (int32_t)p.M;
+    g.N = (int32_t)p.N;
+    g.K = (int32_t)p.K;
+    g.grid_m = (int32_t)gm;
+    g.grid_n = (int32_t)gn;
+    g.group_m = cfg.group_m;
+    g.xcd_remap = cfg.xcd_remap;
+    g.num_xcd = device_info().num_xcd;
+    g.out_dtype = p.out;
+    g.sam = p.sam;
+    g.sak = p.sak;
+    g.sbk = p.sbk;
+    g.sbn = p.sbn;
+    g.scm = p.scm;
+    g.scn = p.scn;
+    const hipError_t err = e->launch(g, stream);
+    if (err != hipSuccess) return fail(DG_ERR_HIP, "launch of %s failed: %s", e->name, hipGetErrorString(err));
+    return DG_OK;
+}
+
+Problem make_problem(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                     int64_t sbk, int64_t sbn, const void *C, int64_t scm, int64_t scn, int in, int out) {
+    return Problem{M, N, K, A, B, C, sam, sak, sbk, sbn, scm, scn, in, out};
+}
+
+void log_choice(const char *what, const Problem &p, const dg_config &c) {
+    if (!log_enabled()) return;
+    fprintf(stderr,
+            "[dg] %s M=%" PRId64 " N=%" PRId64 " K=%" PRId64 " %s->%s: block %dx%dx%d waves %d stages %d variant %d group_m %d xcd %d\n",
+            what, p.M, p.N, p.K, dtype_name(p.in), dtype_name(p.out), c.block_m, c.block_n, c.block_k, c.waves,
+            c.stages, c.variant, c.group_m, c.xcd_remap);
+}
+
+dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_config *chosen, float *best_ms);
+
+}  // namespace
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" {
+
+const char *dg_status_string(dg_status s) {
+    switch (s) {
+    case DG_OK: return "DG_OK";
+    case DG_ERR_INVALID_VALUE: return "DG_ERR_INVALID_VALUE";
+    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED";
+    case DG_ERR_NO_CONFIG: return "DG_ERR_NO_CONFIG";
+    case DG_ERR_HIP: return "DG_ERR_HIP";
+    }
+    return "DG_ERR_UNKNOWN";
+}
+
+const char *dg_last_error(void) { return g_last_error.c_str(); }
+
+dg_status dg_validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                      int64_t sbk, int64_t sbn, const void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
+                      dg_dtype out_dtype) {
+    g_last_error.clear();
+    return validate(make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype));
+}
+
+dg_status dg_select_config(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                           int64_t sbk, int64_t sbn, const void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
+                           dg_dtype out_dtype, dg_config *out, int32_t *from_cache) {
+    g_last_error.clear();
+    if (!out) return fail(DG_ERR_INVALID_VALUE, "out is NULL");
+    // NULL pointers are inspected for alignment only: stand in an aligned address.
+    static const char aligned_stub[16] __attribute__((aligned(16))) = {0};
+    Problem p = make_problem(M, N, K, A ? A : aligned_stub, sam, sak, B ? B : aligned_stub, sbk, sbn,
+                             C ? C : aligned_stub, scm, scn, in_dtype, out_dtype);
+    dg_status s = validate(p);
+    if (s != DG_OK) return s;
+    dg_config c;
+    const bool hit = cache_get(key_of(p), c);
+    if (!hit) c = heuristic(p, device_info().cus);
+    *out = c;
+    if (from_cache) *from_cache = hit ? 1 : 0;
+    return DG_OK;
+}
+
+dg_status dg_gemm_config(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                         int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
+                         dg_dtype out_dtype, void *stream, const dg_config *cfg) {
+    g_last_error.clear();
+    if (!cfg) return fail(DG_ERR_INVALID_VALUE, "cfg is NULL");
+    Problem p = make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype);
+    dg_status s = validate(p);
+    if (s != DG_OK) return s;
+    return launch(p, *cfg, (hipStream_t)stream);
+}
+
+dg_status dg_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                  int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn, dg_dtype in_dtype, dg_dtype out_dtype,
+                  void *stream) {
+    g_last_error.clear();
+    Problem p = make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype);
+    dg_status s = validate(p);
+    if (s != DG_OK) return s;
+    if (M == 0 || N == 0) return DG_OK;
+    dg_config c;
+    if (!cache_get(key_of(p), c)) {
+        static const bool tune_on_miss = [] {
+            const char *v = getenv("DG_AUTOTUNE_ON_MISS");
+            return v && strcmp(v, "1") == 0;
+        }();
+        if (tune_on_miss) return autotune_impl(p, (hipStream_t)stream, 0, nullptr, nullptr);
+        c = heuristic(p, device_info().cus);
+    }
+    log_choice("gemm", p, c);
+    return launch(p, c, (hipStream_t)stream);
+}
+
+dg_status dg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                      int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
+                      dg_dtype out_dtype, void *stream, int32_t repeats, dg_config *chosen, float *best_ms) {
+    g_last_error.clear();
+    Problem p = make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype);
+    dg_status s = validate(p);
+    if (s != DG_OK) return s;
+    return autotune_impl(p, (hipStream_t)stream, repeats, chosen, best_ms);
+}
+
+int32_t dg_num_candidates(dg_dtype in_dtype, dg_dtype out_dtype) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return 0;
+    return (int32_t)candidates(in_dtype, out_dtype).size();
+}
+
+dg_status dg_get_candidate(int32_t i, dg_dtype in_dtype, dg_dtype out_dtype, dg_config *out) {
+    g_last_error.clear();
+    if (!out) return fail(DG_ERR_INVALID_VALUE, "out is NULL");
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(DG_ERR_INVALID_VALUE, "unknown dtype");
+    const auto c = candidates(in_dtype, out_dtype);
+    if (i < 0 || (size_t)i >= c.size()) return fail(DG_ERR_INVALID_VALUE, "candidate index %d out of range", i);
+    *out = c[(size_t)i];
+    return DG_OK;
+}
+
+dg_status dg_tile_coords(int32_t grid_m, int32_t grid_n, int32_t group_m, int32_t xcd_remap, int32_t num_xcd,
+                         int32_t wg, int32_t *pid_m, int32_t *pid_n) {
+    g_last_error.clear();
+    if (grid_m <= 0 || grid_n <= 0 || group_m <= 0 || num_xcd <= 0)
+        return fail(DG_ERR_INVALID_VALUE, "grid, group and XCD counts must be positive");
+    if ((int64_t)grid_m * grid_n >= ((int64_t)1 << 31)) return fail(DG_ERR_INVALID_VALUE, "grid too large");
+    if (wg < 0 || (int64_t)wg >= (int64_t)grid_m * grid_n) return fail(DG_ERR_INVALID_VALUE, "workgroup id out of range");
+    if (!pid_m || !pid_n) return fail(DG_ERR_INVALID_VALUE, "output pointer is NULL");
+    int pm, pn;
+    tile_coords(wg, grid_m, grid_n, group_m, xcd_remap, num_xcd, pm, pn);
+    *pid_m = pm;
+    *pid_n = pn;
+    return DG_OK;
+}
+
+dg_status dg_grid_shape(int64_t M, int64_t N, int64_t K, const dg_config *cfg, int64_t *grid_m, int64_t *grid_n,
+                        int64_t *k_steps) {
+    g_last_error.clear();
+    if (!cfg || !grid_m || !grid_n || !k_steps) return fail(DG_ERR_INVALID_VALUE, "NULL argument");
+    if (M < 0 || N < 0 || K < 0) return fail(DG_ERR_INVALID_VALUE, "negative dimension");
+    if (cfg->block_m <= 0 || cfg->block_n <= 0 || cfg->block_k <= 0)
+        return fail(DG_ERR_INVALID_VALUE, "non-positive block size");
+    *grid_m = (M + cfg->block_m - 1) / cfg->block_m;
+    *grid_n = (N + cfg->block_n - 1) / cfg->block_n;
+    *k_steps = (K + cfg->block_k - 1) / cfg->block_k;
+    return DG_OK;
+}
+
+dg_status dg_cache_clear(void) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache.clear();
+    return DG_OK;
+}
+
+int32_t dg_cache_size(void) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    return (int32_t)g_cache.size();
+}
+
+static const char kCacheHeader[] = "dg-config-cache 1";
+
+dg_status dg_cache_save(const char *path) {
+    g_last_error.clear();
+    if (!path) return fail(DG_ERR_INVALID_VALUE, "path is NULL");
+    std::map<Key, dg_config> snapshot;
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        snapshot = g_cache;
+    }
+    FILE *f = fopen(path, "w");
+    if (!f) return fail(DG_ERR_INVALID_VALUE, "cannot open %s for writing", path);
+    fprintf(f, "%s\n", kCacheHeader);
+    for (const auto &kv : snapshot) {
+        const Key &k = kv.first;
+        const dg_config &c = kv.second;
+        fprintf(f, "%" PRId64 " %" PRId64 " %" PRId64 " %d %d %d %d %d  %d %d %d %d %d %d %d %d\n", k.M, k.N, k.K,
+                k.in, k.out, k.la, k.lb, k.lc, c.block_m, c.block_n, c.block_k, c.group_m, c.waves, c.stages,
+                c.variant, c.xcd_remap);
+    }
+    const bool ok = fclose(f) == 0;
+    return ok ? DG_OK : fail(DG_ERR_INVALID_VALUE, "error writing %s", path);
+}
+
+dg_status dg_cache_load(const char *path) {
+    g_last_error.clear();
+    if (!path) return fail(DG_ERR_INVALID_VALUE, "path is NULL");
+    FILE *f = fopen(path, "r");
+    if (!f) return fail(DG_ERR_INVALID_VALUE, "cannot open %s", path);
+    char line[512];
+    if (!fgets(line, sizeof(line), f) || strncmp(line, kCacheHeader, sizeof(kCacheHeader) - 1) != 0) {
+        fclose(f);
+        return fail(DG_ERR_INVALID_VALUE, "%s is not a config cache file", path);
+    }
+    int bad = 0, good = 0;
+    std::vector<std::pair<Key, dg_config>> entries;
+    while (fgets(line, sizeof(line), f)) {
+        Key k{};
+        dg_config c{};
+        const int n = sscanf(line, "%" SCNd64 " %" SCNd64 " %" SCNd64 " %d %d %d %d %d %d %d %d %d %d %d %d %d", &k.M,
+                             &k.N, &k.K, &k.in, &k.out, &k.la, &k.lb, &k.lc, &c.block_m, &c.block_n, &c.block_k,
+                             &c.group_m, &c.waves, &c.stages, &c.variant, &c.xcd_remap);
+        const bool sane = n == 16 && k.M >= 0 && k.N >= 0 && k.K >= 0 && dtype_ok(k.in) && dtype_ok(k.out) &&
+                          c.block_m > 0 && c.block_n > 0 && c.block_k > 0 && c.group_m > 0;
+        if (!sane) {
+            ++bad;
+            continue;
+        }
+        entries.emplace_back(k, c);
+        ++good;
+    }
+    fclose(f);
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        for (const auto &e : entries) g_cache[e.first] = e.second;
+    }
+    if (bad) {
+        g_last_error = std::to_string(bad) + " malformed line(s) skipped in " + path;
+        if (log_enabled()) fprintf(stderr, "[dg] %s\n", g_last_error.c_str());
+    }
+    return DG_OK;
+}
+
+}  // extern "C"
+
+namespace dg {
+namespace {
+
+dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_config *chosen, float *best_ms) {
+    if (repeats <= 0) repeats = 10;
+    if (p.M == 0 || p.N == 0) {
+        dg_config c = heuristic(p, device_info().cus);
+        if (chosen) *chosen = c;
+        if (best_ms) *best_ms = 0.0f;
+        return DG_OK;
+    }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return fail(DG_ERR_HIP, "hipEventCreate failed");
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return fail(DG_ERR_HIP, "hipEventCreate failed");
+    }
+    const auto cands = candidates(p.in, p.out);
+    dg_config best{};
+    float best_t = 0.0f;
+    bool have = false;
+    dg_status st = DG_OK;
+    std::vector<float> times;
+    for (const auto &c : cands) {
+        if (!find_kernel(c, p)) continue;
+        bool ok = true;
+        for (int w = 0; w < 2 && ok; ++w) ok = launch(p, c, stream) == DG_OK;
+        times.clear();
+        for (int r = 0; r < repeats && ok; ++r) {
+            ok = hipEventRecord(e0, stream) == hipSuccess && launch(p, c, stream) == DG_OK &&
+                 hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+            float ms = 0.0f;
+            ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+            times.push_back(ms);
+        }
+        if (!ok) {
+            st = fail(DG_ERR_HIP, "autotune: candidate %dx%dx%d failed: %s", c.block_m, c.block_n, c.block_k,
+                      g_last_error.c_str());
+            break;
+        }
+        std::sort(times.begin(), times.end());
+        const float med = times[times.size() / 2];
+        if (log_enabled())
+            fprintf(stderr, "[dg] autotune %dx%dx%d w%d g%d xcd%d: %.4f ms\n", c.block_m, c.block_n, c.block_k,
+                    c.waves, c.group_m, c.xcd_remap, med);
+        if (!have || med < best_t) {
+            best = c;
+            best_t = med;
+            have = true;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != DG_OK) return st;
+    if (!have) return fail(DG_ERR_UNSUPPORTED, "no candidate kernel for %s -> %s", dtype_name(p.in), dtype_name(p.out));
+    cache_put(key_of(p), best);
+    log_choice("autotune winner", p, best);
+    st = launch(p, best, stream);
+    if (st != DG_OK) return st;
+    if (hipStreamSynchronize(stream) != hipSuccess) return fail(DG_ERR_HIP, "hipStreamSynchronize failed");
+    if (chosen) *chosen = best;
+    if (best_ms) *best_ms = best_t;
+    return DG_OK;
+}
+
+}  // namespace
+}  // namespace dg

@@ -1,0 +1,397 @@
+// Device code of the dense GEMM library (gfx950 / CDNA4).
+//
+// Two kernel families, both "one workgroup per BLOCK_M x BLOCK_N tile of C,
+// walk K in BLOCK_K slices, accumulate in fp32, mask ragged edges"
+// ("用 Triton 写 GPU Kernel：从 Vector Add、Softmax 到 MatMul" §3.2-§3.4 and
+// §4.5-§4.6; "Triton：04 Matmul、Autotune 与 PyTorch 集成", the tile view):
+//
+//  gemm_simt  -- scalar fp32 FMA over LDS tiles. Any dtype pair, any strides
+//                and alignment. Used for fp32 inputs and as the fallback.
+//  gemm_mfma  -- fp16/bf16 inputs on v_mfma_f32_32x32x16 matrix cores with
+//                fp32 accumulators, a two-buffer LDS pipeline (slice s+1 is
+//                fetched while slice s is multiplied), padded LDS rows, and a
+//                masked, dtype-converting epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg_internal.hpp"
+
+namespace dg {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---- element conversions -----------------------------------------------------
+
+// Storage tags: the element type of A/B/C in memory.
+struct F32 { using storage = float; static constexpr int code = DG_F32; };
+struct F16 { using storage = uint16_t; static constexpr int code = DG_F16; };
+struct BF16 { using storage = uint16_t; static constexpr int code = DG_BF16; };
+
+template <typename T> __device__ __forceinline__ float to_f32(typename T::storage v);
+template <> __device__ __forceinline__ float to_f32<F32>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<F16>(uint16_t v) {
+    return (float)__builtin_bit_cast(_Float16, v);
+}
+template <> __device__ __forceinline__ float to_f32<BF16>(uint16_t v) {
+    return __builtin_bit_cast(float, (uint32_t)v << 16);  // bf16 is the top half of an fp32
+}
+
+// fp32 -> storage, round to nearest even (the hardware conversions).
+template <typename T> __device__ __forceinline__ typename T::storage from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<F32>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<F16>(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+template <> __device__ __forceinline__ uint16_t from_f32<BF16>(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// ============================================================================
+// gemm_simt: 256 threads, a 16 x 16 thread grid, each thread RM x RN outputs.
+// ============================================================================
+template <typename TI, typename TO, int BM, int BN, int BK>
+__global__ __launch_bounds__(256) void gemm_simt(GemmArgs g) {
+    constexpr int T = 256;
+    constexpr int RM = BM / 16, RN = BN / 16;
+    static_assert(BM % 16 == 0 && BN % 16 == 0, "tile must be a multiple of the 16x16 thread grid");
+    __shared__ float As[BK][BM + 1];
+    __shared__ float Bs[BK][BN + 1];
+
+    int pm, pn;
+    tile_coords(blockIdx.x, g.grid_m, g.grid_n, g.group_m, g.xcd_remap, g.num_xcd, pm, pn);
+    const int m0 = pm * BM, n0 = pn * BN;
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    using SI = typename TI::storage;
+    using SO = typename TO::storage;
+    const SI *A = static_cast<const SI *>(g.A);
+    const SI *B = static_cast<const SI *>(g.B);
+    SO *C = static_cast<SO *>(g.C);
+
+    float acc[RM][RN];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) acc[i][j] = 0.0f;
+
+    for (int k0 = 0; k0 < g.K; k0 += BK) {
+        // Stage A[m0:m0+BM, k0:k0+BK] and B[k0:k0+BK, n0:n0+BN]; out-of-view
+        // elements are zero and are not read.
+        for (int e = tid; e < BM * BK; e += T) {
+            const int r = e / BK, kk = e % BK;
+            const int gm = m0 + r, gk = k0 + kk;
+            float v = 0.0f;
+            if (gm < g.M && gk < g.K) v = to_f32<TI>(A[(int64_t)gm * g.sam + (int64_t)gk * g.sak]);
+            As[kk][r] = v;
+        }
+        for (int e = tid; e < BK * BN; e += T) {
+            const int kk = e / BN, c = e % BN;
+            const int gk = k0 + kk, gn = n0 + c;
+            float v = 0.0f;
+            if (gk < g.K && gn < g.N) v = to_f32<TI>(B[(int64_t)gk * g.sbk + (int64_t)gn * g.sbn]);
+            Bs[kk][c] = v;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[RM], b[RN];
+#pragma unroll
+            for (int i = 0; i < RM; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < RN; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+        const int gm = m0 + ty + 16 * i;
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+            const int gn = n0 + tx + 16 * j;
+            if (gm < g.M && gn < g.N) C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(acc[i][j]);
+        }
+    }
+}
+
+// ============================================================================
+// gemm_mfma
+// ============================================================================
+
+// v_mfma_f32_32x32x16_{bf16,f16}: D[32x32] += A[32x16] * B[16x32].
+// Operand registers (8 x 16-bit per lane): lane l holds A[l % 32][8*(l/32) + e]
+// and B[8*(l/32) + e][l % 32], e = 0..7. The k assignment only has to agree
+// between A and B. Result: lane l, register r holds
+// D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+template <typename TI> struct Mfma;
+template <> struct Mfma<BF16> {
+    static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<F16> {
+    static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+
+// Pack/unpack 8 x 16-bit values <-> one 16-byte register.
+__device__ __forceinline__ u32x4 pack8(const uint16_t (&v)[8]) {
+    u32x4 r;
+    r.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+    r.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+    r.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+    r.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+    return r;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const u32x4 &v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// 8x8 transpose of 16-bit elements: in[j] holds row j (8 elements), out[i]
+// holds column i. v_perm_b32 selectors pick the low (even column) or high
+// (odd column) halves of two input dwords.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t d[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            d[p] = __builtin_amdgcn_perm(dword_of(in[2 * p + 1], i >> 1), dword_of(in[2 * p], i >> 1), sel);
+        out[i] = u32x4{d[0], d[1], d[2], d[3]};
+    }
+}
+
+// Fetches one operand tile (ROWS x BK, rows = M for A or N for B) from
+// global memory into registers, then writes it to LDS as [ROWS][LDK] with k
+// contiguous. Elements outside the operand's view (row >= rows_valid or
+// k >= K) become +0 and are never read.
+template <int ROWS, int BK, int LDK, int T, int MODE>
+struct TileLoader {
+    static constexpr int KCH = BK / 8;                   // 8-element k-chunks per row
+    static constexpr int NCH = ROWS * KCH;               // chunks per tile (KC, GN)
+    static constexpr int PER = (NCH + T - 1) / T;
+    static constexpr int NBL = (ROWS / 8) * KCH;         // 8x8 blocks per tile (RC)
+    static constexpr int PERB = (NBL + T - 1) / T;
+    static constexpr int NREG = MODE == LD_RC ? PERB * 8 : PER;
+
+    u32x4 reg[NREG];
+    const uint16_t *base;  // element (row0, k = 0) of the operand
+    int64_t srow, sk;      // element strides along rows and along k
+    int rows_valid;        // rows of the tile inside the operand
+    int K;
+
+    __device__ __forceinline__ void load(int tid, int k0) {
+        if constexpr (MODE == LD_RC) {
+#pragma unroll
+            for (int b = 0; b < PERB; ++b) {
+                const int q = b * T + tid;
+                u32x4 raw[8];
+                const int kb = q % KCH, rb = q / KCH;
+                const int r0 = rb * 8;
+                const bool qok = (NBL % T == 0) || q < NBL;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int k = k0 + kb * 8 + j;
+                    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                    if (qok && k < K) {
+                        const uint16_t *p = base + (int64_t)k * sk + r0;
+                        if (r0 + 8 <= rows_valid) {
+                            v = *reinterpret_cast<const u32x4 *>(p);
+                        } else if (r0 < rows_valid) {
+                            uint16_t e8[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) e8[e] = (r0 + e < rows_valid) ? p[e] : (uint16_t)0;
+                            v = pack8(e8);
+                        }
+                    }
+                    raw[j] = v;
+                }
+                u32x4 t[8];
+                transpose8x8(raw, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) reg[b * 8 + i] = t[i];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < PER; ++c) {
+                const int q = c * T + tid;
+                const int r = q / KCH, kc = q % KCH;
+                const int k = k0 + kc * 8;
+                const bool ok = ((NCH % T == 0) || q < NCH) && r < rows_valid;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (MODE == LD_KC) {
+                    const uint16_t *p = base + (int64_t)r * srow + k;
+                    if (ok && k + 8 <= K) {
+                        v = *reinterpret_cast<const u32x4 *>(p);
+                    } else if (ok && k < K) {
+                        uint16_t e8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) e8[e] = (k + e < K) ? p[e] : (uint16_t)0;
+                        v = pack8(e8);
+                    }
+                } else {  // LD_GN
+                    if (ok) {
+                        const uint16_t *p = base + (int64_t)r * srow;
+                        uint16_t e8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) e8[e] = (k + e < K) ? p[(int64_t)(k + e) * sk] : (uint16_t)0;
+                        v = pack8(e8);
+                    }
+                }
+                reg[c] = v;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(int tid, uint16_t *lds) const {
+        if constexpr (MODE == LD_RC) {
+#pragma unroll
+            for (int b = 0; b < PERB; ++b) {
+                const int q = b * T + tid;
+                if ((NBL % T == 0) || q < NBL) {
+                    const int kb = q % KCH, rb = q / KCH;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        *reinterpret_cast<u32x4 *>(lds + (rb * 8 + i) * LDK + kb * 8) = reg[b * 8 + i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < PER; ++c) {
+                const int q = c * T + tid;
+                if ((NCH % T == 0) || q < NCH) {
+                    const int r = q / KCH, kc = q % KCH;
+                    *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = reg[c];
+                }
+            }
+        }
+    }
+};
+
+template <typename TO>
+__device__ __forceinline__ void store_c(void *C, int64_t off, float v) {
+    static_cast<typename TO::storage *>(C)[off] = from_f32<TO>(v);
+}
+
+// WM x WN waves, each owning a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
+    constexpr int T = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int LDK = BK + 8;  // row pitch (elements): +16 B breaks the bank pattern of 128 B rows
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
+    static_assert(BM % 8 == 0 && BN % 8 == 0, "8-row blocks");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * LDK];
+
+    int pm, pn;
+    tile_coords(blockIdx.x, g.grid_m, g.grid_n, g.group_m, g.xcd_remap, g.num_xcd, pm, pn);
+    const int m0 = pm * BM, n0 = pn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    TileLoader<BM, BK, LDK, T, LA> la;
+    TileLoader<BN, BK, LDK, T, LB> lb;
+    const uint16_t *A = static_cast<const uint16_t *>(g.A);
+    const uint16_t *B = static_cast<const uint16_t *>(g.B);
+    la.base = A + (int64_t)m0 * g.sam;
+    la.srow = g.sam;
+    la.sk = g.sak;
+    la.rows_valid = min(BM, g.M - m0);
+    la.K = g.K;
+    lb.base = B + (int64_t)n0 * g.sbn;
+    lb.srow = g.sbn;
+    lb.sk = g.sbk;
+    lb.rows_valid = min(BN, g.N - n0);
+    lb.K = g.K;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = (g.K + BK - 1) / BK;
+    if (nk > 0) {
+        la.load(tid, 0);
+        lb.load(tid, 0);
+        la.store(tid, lds[0]);
+        lb.store(tid, lds[0] + BM * LDK);
+        __syncthreads();
+    }
+
+    // LDS offsets (elements) of this lane's fragment rows.
+    const int a_row = (wm * WTM + (lane & 31)) * LDK + (lane >> 5) * 8;
+    const int b_row = (BM + wn * WTN + (lane & 31)) * LDK + (lane >> 5) * 8;
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            la.load(tid, (kt + 1) * BK);
+            lb.load(tid, (kt + 1) * BK);
+        }
+        const uint16_t *s = lds[cur];
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(s + a_row + i * 32 * LDK + kk * 16);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const u32x4 *>(s + b_row + j * 32 * LDK + kk * 16);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<TI>::run(af[i], bf[j], acc[i][j]);
+        }
+        if (more) {
+            la.store(tid, lds[cur ^ 1]);
+            lb.store(tid, lds[cur ^ 1] + BM * LDK);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: fp32 accumulators -> C's dtype, masked to C's view.
+    const int row_base = m0 + wm * WTM + 4 * (lane >> 5);
+    const int col_base = n0 + wn * WTN + (lane & 31);
+    const int out = g.out_dtype;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int gn = col_base + j * 32;
+            if (gn >= g.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                if (gm < g.M) {
+                    const int64_t off = (int64_t)gm * g.scm + (int64_t)gn * g.scn;
+                    const float v = acc[i][j][r];
+                    if (out == DG_BF16) store_c<BF16>(g.C, off, v);
+                    else if (out == DG_F16) store_c<F16>(g.C, off, v);
+                    else store_c<F32>(g.C, off, v);
+                }
+            }
+        }
+}
+
+}  // namespace dg

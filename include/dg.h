@@ -1,0 +1,197 @@
+/*
+ * dg.h -- C-ABI of an MI355X (gfx950) tiled dense matrix multiply.
+ *
+ *   C[i][j] = round_out( sum_{k<K} A[i][k] * B[k][j] ),  0 <= i < M, 0 <= j < N
+ *
+ * The operation is the product of an M x K matrix and a K x N matrix
+ * ("用 Triton 写 GPU Kernel：从 Vector Add、Softmax 到 MatMul", §3.1: an output
+ * element is a row of A times a column of B, summed over K). Each workgroup
+ * owns one BLOCK_M x BLOCK_N tile of C and walks K in BLOCK_K slices
+ * (same page §3.2-§3.4; "Triton：04 Matmul、Autotune 与 PyTorch 集成", the tile
+ * view), accumulating in fp32 ("I Wrote a GPU Matmul Kernel From Scratch in
+ * Triton", the finding that fp32 accumulation matters; load fp16, accumulate
+ * fp32, store fp16 or fp32).
+ *
+ * Conventions for every entry point that takes a problem:
+ *  - Pointers A, B, C are DEVICE pointers (HIP device memory), owned by the
+ *    caller. The library never allocates device memory on the dg_gemm path
+ *    and never frees caller memory.
+ *  - Strides are in ELEMENTS, not bytes ("用 Triton 写 GPU Kernel" §4.1): A[i][k]
+ *    is at A + i*stride_am + k*stride_ak, B[k][j] at B + k*stride_bk +
+ *    j*stride_bn, C[i][j] at C + i*stride_cm + j*stride_cn. This is the
+ *    stride-argument form of the teaching kernel in "Triton：04 Matmul…".
+ *    A and B strides must be >= 0 (0 is allowed: a broadcast operand). C
+ *    strides must be >= 1 and C's index map injective (no two (i, j) share
+ *    an element).
+ *  - Accumulation is fp32; inputs of fp16/bf16 give exact products. The
+ *    output is rounded to out_dtype with round-to-nearest-even (the pages
+ *    cast the fp32 accumulator to the output type after the K loop).
+ *  - A and B are read only inside their M x K / K x N views; elements past a
+ *    ragged edge count as zero (the masked load with other = 0 of the
+ *    pages' kernels). Every element of C's M x N view is written exactly
+ *    once; nothing else in C's allocation is written. C is overwritten
+ *    (there is no alpha/beta).
+ *  - M == 0 or N == 0: returns DG_OK and launches nothing. K == 0: C is
+ *    filled with +0 (the empty sum).
+ *  - stream is a hipStream_t (NULL = the legacy default stream). Work is
+ *    enqueued on it; dg_gemm returns without synchronising the host.
+ *  - On any error the call returns a status != DG_OK, enqueues nothing, and
+ *    dg_last_error() describes it (thread-local).
+ *  - All entry points are thread-safe; the config cache is mutex-guarded.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_dtype {
+    DG_F32 = 0,   /* IEEE binary32 */
+    DG_F16 = 1,   /* IEEE binary16 */
+    DG_BF16 = 2   /* bfloat16 (top half of a binary32) */
+} dg_dtype;
+
+typedef enum dg_status {
+    DG_OK = 0,
+    DG_ERR_INVALID_VALUE = 1,  /* bad dimension, pointer, stride, alignment or dtype */
+    DG_ERR_UNSUPPORTED = 2,    /* valid request this build has no kernel for */
+    DG_ERR_NO_CONFIG = 3,      /* explicit config invalid for this problem/dtype */
+    DG_ERR_HIP = 4             /* a HIP runtime call failed */
+} dg_status;
+
+/* Kernel families (dg_config.variant). */
+enum {
+    DG_VARIANT_SIMT = 0,  /* LDS-tiled fp32 FMA kernel: any dtype pair, any strides */
+    DG_VARIANT_MFMA = 1   /* fp16/bf16 inputs: v_mfma_f32_32x32x16 tiles, fp32 accumulators */
+};
+
+/*
+ * One kernel configuration. The tile sizes, waves and stages name a kernel
+ * instantiation compiled into the library (block sizes are compile-time, as
+ * in the pages' constexpr BLOCK_M/N/K); group_m and xcd_remap are read at
+ * launch time.
+ *  block_m, block_n, block_k: tile of C per workgroup and K slice per step.
+ *  group_m:   rows of tiles per group in the group-major launch order
+ *             ("I Wrote a GPU Matmul Kernel From Scratch in Triton", Step 4);
+ *             1 gives plain row-major tile order.
+ *  waves:     64-lane wavefronts per workgroup (the num_warps analogue).
+ *  stages:    LDS buffers in the K pipeline (num_stages analogue; 2 = load
+ *             slice s+1 while slice s is multiplied).
+ *  variant:   DG_VARIANT_*.
+ *  xcd_remap: 1 = reorder workgroup ids so the tiles dispatched to one XCD
+ *             (one L2) are consecutive in the group-major order.
+ */
+typedef struct dg_config {
+    int32_t block_m, block_n, block_k;
+    int32_t group_m;
+    int32_t waves;
+    int32_t stages;
+    int32_t variant;
+    int32_t xcd_remap;
+} dg_config;
+
+/*
+ * C = A @ B with the library's choice of kernel: the cached config for this
+ * problem key if one exists (see dg_autotune), else a built-in heuristic.
+ * Never benchmarks, so its cost is one kernel launch (unless the
+ * environment sets DG_AUTOTUNE_ON_MISS=1, which autotunes on a cache miss).
+ * Arguments: problem sizes; the three device pointers and their element
+ * strides; the input dtype (shared by A and B) and the output dtype; stream.
+ */
+dg_status dg_gemm(int64_t M, int64_t N, int64_t K,
+                  const void *A, int64_t stride_am, int64_t stride_ak,
+                  const void *B, int64_t stride_bk, int64_t stride_bn,
+                  void *C, int64_t stride_cm, int64_t stride_cn,
+                  dg_dtype in_dtype, dg_dtype out_dtype, void *stream);
+
+/*
+ * Same as dg_gemm with an explicit configuration (tests, ablations). A
+ * config that names no compiled kernel, or one that cannot run this
+ * problem's dtype pair, returns DG_ERR_NO_CONFIG. The problem size is never
+ * a reason to reject a config: ragged edges and K < block_k are masked.
+ */
+dg_status dg_gemm_config(int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t stride_am, int64_t stride_ak,
+                         const void *B, int64_t stride_bk, int64_t stride_bn,
+                         void *C, int64_t stride_cm, int64_t stride_cn,
+                         dg_dtype in_dtype, dg_dtype out_dtype, void *stream,
+                         const dg_config *cfg);
+
+/*
+ * Benchmark every candidate config for this problem on the caller's buffers
+ * (C is overwritten many times), keep the fastest (lowest median of
+ * `repeats` timed launches after warm-up; ties go to the earlier candidate),
+ * store it in the cache under the problem key, and run it once more so C
+ * holds its result. Synchronises `stream`. This is the pages' autotune:
+ * measure candidate configs for a shape key and cache the winner
+ * ("Triton：04 Matmul、Autotune 与 PyTorch 集成", what autotune chooses).
+ * chosen / best_ms may be NULL. repeats <= 0 selects a default.
+ */
+dg_status dg_autotune(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t stride_am, int64_t stride_ak,
+                      const void *B, int64_t stride_bk, int64_t stride_bn,
+                      void *C, int64_t stride_cm, int64_t stride_cn,
+                      dg_dtype in_dtype, dg_dtype out_dtype, void *stream,
+                      int32_t repeats, dg_config *chosen, float *best_ms);
+
+/*
+ * The config dg_gemm would use, without any GPU work. The pointers are only
+ * inspected for alignment (they may be NULL: then taken as 16-byte aligned).
+ * *from_cache (may be NULL) is set to 1 if the config came from the cache.
+ * The cache key is (M, N, K) plus the dtypes, each operand's layout class
+ * and the vector-alignment class.
+ */
+dg_status dg_select_config(int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t stride_am, int64_t stride_ak,
+                           const void *B, int64_t stride_bk, int64_t stride_bn,
+                           const void *C, int64_t stride_cm, int64_t stride_cn,
+                           dg_dtype in_dtype, dg_dtype out_dtype,
+                           dg_config *out, int32_t *from_cache);
+
+/* Autotune candidates for a dtype pair: count, and the i-th (0-based). */
+int32_t dg_num_candidates(dg_dtype in_dtype, dg_dtype out_dtype);
+dg_status dg_get_candidate(int32_t i, dg_dtype in_dtype, dg_dtype out_dtype, dg_config *out);
+
+/* Check a full argument list exactly as dg_gemm does, without launching. */
+dg_status dg_validate(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t stride_am, int64_t stride_ak,
+                      const void *B, int64_t stride_bk, int64_t stride_bn,
+                      const void *C, int64_t stride_cm, int64_t stride_cn,
+                      dg_dtype in_dtype, dg_dtype out_dtype);
+
+/*
+ * Launch-order helper (host side of the device tile map): the C tile
+ * (*pid_m, *pid_n) that workgroup `wg` computes, for a grid of
+ * grid_m x grid_n tiles, group_m rows per group (group-major order, "I Wrote
+ * a GPU Matmul Kernel From Scratch in Triton", Step 4) and, if xcd_remap, the
+ * XCD-aware renumbering over num_xcd XCDs. Returns DG_ERR_INVALID_VALUE for
+ * wg outside [0, grid_m*grid_n) or non-positive sizes.
+ */
+dg_status dg_tile_coords(int32_t grid_m, int32_t grid_n, int32_t group_m, int32_t xcd_remap,
+                         int32_t num_xcd, int32_t wg, int32_t *pid_m, int32_t *pid_n);
+
+/*
+ * Grid a config launches for a problem: tiles along M and N, and K steps
+ * (ceil divisions, "用 Triton 写 GPU Kernel" §3.2 and §4.6).
+ */
+dg_status dg_grid_shape(int64_t M, int64_t N, int64_t K, const dg_config *cfg,
+                        int64_t *grid_m, int64_t *grid_n, int64_t *k_steps);
+
+/* Config cache: clear; save to / load from a text file (one key per line). */
+dg_status dg_cache_clear(void);
+dg_status dg_cache_save(const char *path);
+dg_status dg_cache_load(const char *path);
+int32_t dg_cache_size(void);
+
+/* Static description of a status code, and the calling thread's last error. */
+const char *dg_status_string(dg_status s);
+const char *dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

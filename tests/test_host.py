@@ -1,0 +1,207 @@
+"""CPU tests of the C-ABI library's host logic (no GPU work is started).
+
+The library must load and export every entry point declared in include/dg.h;
+argument validation, launch order, grid arithmetic, config selection and the
+config cache are exercised through the C-ABI itself.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import dense_gemm_07_amd as dg
+from conftest import ROOT, load_golden, load_grid_counts
+
+F32, F16, BF16 = dg.DG_F32, dg.DG_F16, dg.DG_BF16
+OK, INVALID, NO_CONFIG = 0, 1, 3
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "dg.h")).read()
+    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dg.library()
+    names = declared_symbols()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dg.h but not exported"
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(dg, "_lib", None)
+    monkeypatch.setattr(dg, "LIB", "/nonexistent/libdg.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        dg.library()
+
+
+def test_status_strings():
+    lib = dg.library()
+    assert lib.dg_status_string(0) == b"DG_OK"
+    assert lib.dg_status_string(3) == b"DG_ERR_NO_CONFIG"
+
+
+# ---- launch order -------------------------------------------------------------
+
+def test_group_major_layout_from_the_page():
+    g = load_golden("p1_s4_group_major.txt")
+    for label, group in (("ROWMAJOR", 1), ("GROUP2", 2)):
+        grid = [[None] * 4 for _ in range(4)]
+        for wg in range(16):
+            m, n = dg.tile_coords(4, 4, group, 0, 8, wg)
+            grid[m][n] = wg
+        assert grid == g[label], label
+
+
+@pytest.mark.parametrize("xcd", [0, 1])
+def test_tile_map_is_a_bijection(xcd):
+    for gm, gn in itertools.product([1, 2, 3, 5, 8, 13, 16, 17], repeat=2):
+        for group in (1, 2, 3, 4, 8, 16):
+            for nx in ((1, 8) if xcd else (8,)):
+                seen = set()
+                for wg in range(gm * gn):
+                    m, n = dg.tile_coords(gm, gn, group, xcd, nx, wg)
+                    assert 0 <= m < gm and 0 <= n < gn
+                    seen.add((m, n))
+                assert len(seen) == gm * gn, (gm, gn, group, xcd, nx)
+
+
+def test_xcd_remap_gives_each_xcd_a_consecutive_run():
+    # 16 x 16 tiles over 8 XCDs: with group 4, the 32 ids dispatched to one
+    # XCD (wg % 8 == x) cover a compact 4-row x 8-column block of tiles.
+    for x in range(8):
+        tiles = {dg.tile_coords(16, 16, 4, 1, 8, wg) for wg in range(x, 256, 8)}
+        rows = {m for m, _ in tiles}
+        cols = {n for _, n in tiles}
+        assert len(tiles) == 32 and len(rows) == 4 and len(cols) == 8, (x, sorted(tiles))
+
+
+def test_tile_coords_rejects_bad_arguments():
+    for args in [(0, 4, 1, 0, 8, 0), (4, 4, 0, 0, 8, 0), (4, 4, 1, 0, 8, 16), (4, 4, 1, 0, 8, -1)]:
+        with pytest.raises(dg.DGError):
+            dg.tile_coords(*args)
+
+
+# ---- grid arithmetic (pages' counts) ------------------------------------------
+
+def test_grid_counts_from_the_pages():
+    for M, N, K, BM, BN, BK, gm, gn, ks, oob_r, oob_c, oob_k in load_grid_counts():
+        cfg = dg.Config(BM, BN, BK, 1, 4, 1, dg.VARIANT_SIMT, 0)
+        got_m, got_n, got_k = dg.grid_shape(M, N, max(K, 0), cfg)
+        assert (got_m, got_n) == (gm, gn)
+        if ks >= 0:
+            assert got_k == ks
+        if oob_r >= 0:
+            assert got_m * BM - M == oob_r
+        if oob_c >= 0:
+            assert got_n * BN - N == oob_c
+        if oob_k >= 0:
+            assert got_k * BK - K == oob_k
+    # "用 Triton 写 GPU Kernel" §3.4: 16 programs x 3 rounds = 48 small products
+    gm, gn, ks = dg.grid_shape(8, 8, 6, dg.Config(2, 2, 2, 1, 4, 1, 0, 0))
+    assert gm * gn * ks == 48
+
+
+# ---- validation -----------------------------------------------------------------
+
+P = 4096  # a stand-in device address (16-byte aligned); nothing is dereferenced
+
+
+def v(M=4, N=4, K=4, a=P, sa=(4, 1), b=P, sb=(4, 1), c=P, sc=(4, 1), i=BF16, o=BF16):
+    return dg.validate(M, N, K, a, sa, b, sb, c, sc, i, o)
+
+
+def test_validate_accepts_good_arguments():
+    assert v() == OK
+    assert v(sa=(0, 0), sb=(0, 0)) == OK               # broadcast operands are allowed
+    assert v(sb=(1, 4)) == OK                           # column-major B
+    assert v(M=0, a=0, c=0) == OK                       # empty problem needs no pointers
+    assert v(K=0, a=0, b=0) == OK                       # K = 0 writes zeros into C
+    assert v(M=2, N=2, sc=(3, 2)) == OK                 # offsets 0,2,3,5: no overlap
+    assert v(i=F32, o=F16, a=P + 4, b=P + 8) == OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=-1), dict(K=-1),
+    dict(a=0), dict(b=0), dict(c=0),
+    dict(sa=(-4, 1)), dict(sb=(4, -1)),
+    dict(sc=(0, 1)), dict(sc=(4, 0)),
+    dict(sc=(1, 1)), dict(sc=(2, 1)), dict(M=3, N=3, sc=(2, 1)),
+    dict(a=P + 1), dict(c=P + 1), dict(i=F32, a=P + 2),
+    dict(i=7), dict(o=-1),
+])
+def test_validate_rejects(kw):
+    assert v(**kw) == INVALID
+
+
+def test_validate_rejects_huge_dims():
+    assert v(M=1 << 31) != OK
+
+
+# ---- config selection ----------------------------------------------------------
+
+def test_heuristic_choices():
+    c, hit = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (4096, 1), (4096, 1), BF16, BF16)
+    assert not hit and c.variant == dg.VARIANT_MFMA and (c.block_m, c.block_n) == (256, 256)
+    c, _ = dg.select_config_raw(26, 26, 26, (26, 1), (26, 1), (26, 1), F32, F32)
+    assert c.variant == dg.VARIANT_SIMT
+    c, _ = dg.select_config_raw(1024, 1024, 1024, (1024, 1), (1024, 1), (1024, 1), F16, F16)
+    assert c.variant == dg.VARIANT_MFMA and (1024 // c.block_m) * (1024 // c.block_n) >= 256
+
+
+def test_candidates_are_distinct_and_complete():
+    for i, o in itertools.product([F32, F16, BF16], repeat=2):
+        cands = dg.candidates(i, o)
+        assert cands, (i, o)
+        keys = {tuple(c.as_dict().values()) for c in cands}
+        assert len(keys) == len(cands)
+        if i != F32:
+            assert all(c.variant == dg.VARIANT_MFMA for c in cands)
+            assert {c.group_m for c in cands} >= {1, 8} and {c.xcd_remap for c in cands} == {0, 1}
+
+
+def test_candidate_index_out_of_range():
+    lib = dg.library()
+    n = lib.dg_num_candidates(BF16, BF16)
+    assert lib.dg_get_candidate(n, BF16, BF16, ctypes.byref(dg.Config())) == INVALID
+    assert lib.dg_num_candidates(9, BF16) == 0
+
+
+# ---- config cache ----------------------------------------------------------------
+
+def test_cache_load_select_save_roundtrip(tmp_path):
+    dg.cache_clear()
+    # key: M N K in out la lb lc | block_m block_n block_k group_m waves stages variant xcd
+    f = tmp_path / "cache.txt"
+    f.write_text("dg-config-cache 1\n"
+                 "4096 4096 4096 2 2 0 1 0  128 128 64 4 4 2 1 0\n"
+                 "this line is garbage\n")
+    dg.cache_load(str(f))
+    assert dg.cache_size() == 1
+    assert b"malformed" in dg.library().dg_last_error()
+    c, hit = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (4096, 1), (4096, 1), BF16, BF16)
+    assert hit and (c.block_m, c.block_n, c.group_m, c.xcd_remap) == (128, 128, 4, 0)
+    # a different layout class of B is a different key
+    _, hit2 = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (1, 4096), (4096, 1), BF16, BF16)
+    assert not hit2
+    out = tmp_path / "saved.txt"
+    dg.cache_save(str(out))
+    lines = out.read_text().splitlines()
+    assert lines[0] == "dg-config-cache 1" and len(lines) == 2
+    dg.cache_clear()
+    assert dg.cache_size() == 0
+    dg.cache_load(str(out))
+    assert dg.cache_size() == 1
+    dg.cache_clear()
+
+
+def test_cache_load_rejects_foreign_file(tmp_path):
+    f = tmp_path / "x.txt"
+    f.write_text("not a cache\n")
+    with pytest.raises(dg.DGError):
+        dg.cache_load(str(f))
+    with pytest.raises(dg.DGError):
+        dg.cache_load(str(tmp_path / "missing.txt"))
