@@ -96,7 +96,10 @@ def main():
 
     import dense_gemm_07_amd as dg
     from dense_gemm_07_amd import inputs
+    from dense_gemm_07_amd.build import LIB, build
 
+    if not os.path.exists(LIB):
+        build()
     w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -101,13 +101,14 @@ dg_status validate(const Problem &p) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Load mode of an operand viewed as rows x K with strides (srow, sk), for the
-// 16-bit MFMA kernels (8 elements = 16 bytes per vector).
+// 16-bit MFMA kernels. The vector modes move 16-byte chunks (8 elements) that
+// are either wholly inside the operand's view or wholly outside it, and
+// address a tile with 31-bit byte offsets (the largest tile has 256 rows).
 int load_mode(const void *base, int64_t rows, int64_t K, int64_t srow, int64_t sk) {
     if (!aligned16(base)) return LD_GN;
-    const bool row_ok = rows <= 1 || srow % 8 == 0;
-    const bool k_ok = K <= 1 || sk % 8 == 0;
-    if (sk == 1 && row_ok) return LD_KC;
-    if (srow == 1 && k_ok) return LD_RC;
+    const int64_t lim = (int64_t)1 << 30;  // elements: 2 bytes each stays below 2^31
+    if (sk == 1 && K % 8 == 0 && (rows <= 1 || srow % 8 == 0) && 256 * srow + K < lim) return LD_KC;
+    if (srow == 1 && rows % 8 == 0 && (K <= 1 || sk % 8 == 0) && K * sk + 256 < lim) return LD_RC;
     return LD_GN;
 }
 
@@ -119,8 +120,16 @@ const std::vector<KernelEntry> &registry() {
     static const std::vector<KernelEntry> reg = [] {
         std::vector<KernelEntry> r;
         register_simt(r);
-        register_mfma_bf16(r);
-        register_mfma_f16(r);
+        register_mfma_bf16_kc_rc(r);
+        register_mfma_bf16_kc_kc(r);
+        register_mfma_bf16_rc_rc(r);
+        register_mfma_bf16_rc_kc(r);
+        register_mfma_bf16_gn(r);
+        register_mfma_f16_kc_rc(r);
+        register_mfma_f16_kc_kc(r);
+        register_mfma_f16_rc_rc(r);
+        register_mfma_f16_rc_kc(r);
+        register_mfma_f16_gn(r);
         return r;
     }();
     return reg;

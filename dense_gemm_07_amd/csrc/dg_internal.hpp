@@ -30,8 +30,8 @@ struct GemmArgs {
 // How an operand tile is fetched from global memory. The operand is viewed
 // as rows x K (rows = M for A, N for B) with a row stride and a k stride.
 enum LoadMode : int32_t {
-    LD_KC = 0,  // k-contiguous (k stride 1), 16-byte aligned rows: 16-byte vector loads
-    LD_RC = 1,  // row-contiguous (row stride 1), 16-byte aligned k-lines: vector loads + 8x8 transpose
+    LD_KC = 0,  // k-contiguous (k stride 1), 16-byte aligned rows, K % 8 == 0
+    LD_RC = 1,  // row-contiguous (row stride 1), 16-byte aligned k-lines, rows % 8 == 0
     LD_GN = 2,  // anything else: element loads through both strides
 };
 
@@ -50,8 +50,15 @@ struct KernelEntry {
 
 // Registration hooks, one per kernel translation unit.
 void register_simt(std::vector<KernelEntry> &out);
-void register_mfma_bf16(std::vector<KernelEntry> &out);
-void register_mfma_f16(std::vector<KernelEntry> &out);
+#define DG_DECLARE_MFMA_HOOKS(t)                               \
+    void register_mfma_##t##_kc_rc(std::vector<KernelEntry> &out); \
+    void register_mfma_##t##_kc_kc(std::vector<KernelEntry> &out); \
+    void register_mfma_##t##_rc_rc(std::vector<KernelEntry> &out); \
+    void register_mfma_##t##_rc_kc(std::vector<KernelEntry> &out); \
+    void register_mfma_##t##_gn(std::vector<KernelEntry> &out);
+DG_DECLARE_MFMA_HOOKS(bf16)
+DG_DECLARE_MFMA_HOOKS(f16)
+#undef DG_DECLARE_MFMA_HOOKS
 
 // ---------------------------------------------------------------------------
 // Tile launch order. A workgroup id is mapped to the C tile it computes:

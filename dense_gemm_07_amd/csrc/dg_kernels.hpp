@@ -394,4 +394,265 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
         }
 }
 
+// ============================================================================
+// gemm_mfma_lds: operands travel global -> LDS directly
+// ============================================================================
+//
+// Each 64-lane buffer_load_dwordx4 ... lds writes 1 KiB of LDS: lane i's 16
+// bytes land at M0 + 16*i. The tile layout is chosen by which global chunk
+// each lane fetches. A buffer offset past num_records reads as zero, which
+// masks rows past M/N and k past K without a branch.
+//
+// Two LDS tile formats:
+//  KTile [ROWS][BK], k contiguous (operand with k stride 1). A 32x32x16
+//        fragment row is one ds_read_b128. The eight 16-byte chunks of a
+//        128-byte row are XOR-swizzled with the row index, so the 8- and
+//        16-lane groups of a ds_read_b128 hit distinct banks.
+//  RTile [BK][ROWS], rows contiguous (operand with row stride 1, e.g. a
+//        row-major B). Fragments come from ds_read_b64_tr_b16, which
+//        transposes within 16-lane groups: lane j of a group receives element
+//        (j % 4) of the 4-element rows addressed by lanes 4e + j/4, e = 0..3.
+//        Chunks are XOR-swizzled by 2*(k % 4), so the four k-lines a group
+//        reads fall on distinct banks.
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr int kOobOffset = (int)0x80000000;  // buffer offset >= num_records: loads zero
+constexpr int kNumRecords = 0x7fffffff;
+constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data format
+
+// s_waitcnt vmcnt(0) (expcnt/lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int ROWS, int BK>
+struct KTile {
+    static_assert(BK == 64, "KTile swizzle assumes 128-byte rows");
+    static constexpr int CPR = BK / 8;            // 16-byte chunks per row
+    static constexpr int RPL = 1024 / (BK * 2);   // rows per 1 KiB wave load
+    static constexpr int NLOADS = ROWS / RPL;
+    static constexpr int BYTES = ROWS * BK * 2;
+    __device__ static __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+    // Element (row, k) of the tile that lane `lane` of wave load `b` fetches (k a multiple of 8).
+    __device__ static __forceinline__ void src(int b, int lane, int &row, int &k) {
+        row = b * RPL + lane / CPR;
+        k = ((lane % CPR) ^ swz(row)) * 8;
+    }
+    // Byte offset in the tile of the 16 bytes holding (row, k..k+7).
+    __device__ static __forceinline__ int at(int row, int k) {
+        return row * (BK * 2) + (((k >> 3) ^ swz(row)) << 4);
+    }
+};
+
+template <int ROWS, int BK>
+struct RTile {
+    static constexpr int CPR = ROWS / 8;          // 16-byte chunks per k-line
+    static_assert(CPR >= 8, "RTile needs at least 64 rows");
+    static constexpr int KPL = 1024 / (ROWS * 2); // k-lines per 1 KiB wave load
+    static_assert(KPL >= 1, "RTile k-line larger than one wave load");
+    static constexpr int NLOADS = BK / KPL;
+    static constexpr int BYTES = ROWS * BK * 2;
+    __device__ static __forceinline__ int swz(int k) { return 2 * (k & 3); }
+    __device__ static __forceinline__ void src(int b, int lane, int &k, int &row) {
+        k = b * KPL + lane / CPR;
+        row = ((lane % CPR) ^ swz(k)) * 8;
+    }
+    // Byte offset of element (k, row); row a multiple of 4 for the 8-byte reads.
+    __device__ static __forceinline__ int at(int k, int row) {
+        return k * (ROWS * 2) + ((((row >> 3) ^ swz(k))) << 4) + ((row & 7) << 1);
+    }
+};
+
+// MFMA operand for rows [r0, r0+32) x k [k0, k0+16): lane l receives
+// (row r0 + l%32, k = k0 + 8*(l/32) + e), e = 0..7.
+template <int ROWS, int BK>
+__device__ __forceinline__ u32x4 frag_from_ktile(const char *tile, int r0, int k0, int lane) {
+    const int row = r0 + (lane & 31);
+    const int k = k0 + ((lane >> 5) << 3);
+    return *reinterpret_cast<const u32x4 *>(tile + KTile<ROWS, BK>::at(row, k));
+}
+
+template <int ROWS, int BK>
+__device__ __forceinline__ u32x4 frag_from_rtile(const char *tile, int r0, int k0, int lane) {
+    // Lane i of 16-lane group q addresses the 4-element line (k0 + 8*(q/2) + i/4 [+4],
+    // r0 + 16*(q%2) + 4*(i%4)); after the transpose lane j of the group holds
+    // rows r0 + 16*(q%2) + j at k = k0 + 8*(q/2) + e.
+    const int q = lane >> 4, i = lane & 15;
+    const int row = r0 + 16 * (q & 1) + 4 * (i & 3);
+    const int k = k0 + 8 * (q >> 1) + (i >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t *)(tile + RTile<ROWS, BK>::at(k, row)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t *)(tile + RTile<ROWS, BK>::at(k + 4, row)));
+    u32x4 r;
+    r.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    r.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+    r.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+    r.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    return r;
+}
+
+// Per-operand state of the direct loads: the buffer descriptor (tile origin,
+// k = 0), each wave load's per-lane byte offset (or kOobOffset), and the
+// k stride in bytes.
+template <int ROWS, int BK, int MODE, int NW>
+struct DirectLoader {
+    using KT = KTile<ROWS, BK>;
+    using RT = RTile<ROWS, BK>;
+    static constexpr int NLOADS = MODE == LD_KC ? KT::NLOADS : RT::NLOADS;
+    static constexpr int PER = NLOADS / NW;
+    static_assert(NLOADS % NW == 0, "wave loads must split evenly over the waves");
+
+    __amdgpu_buffer_rsrc_t rsrc;
+    int voff[PER];
+    int kstride_bytes;
+
+    __device__ __forceinline__ void init(const uint16_t *origin, int64_t srow, int64_t sk, int rows_valid,
+                                         int wave, int lane) {
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)origin, 0, kNumRecords, kRsrcWord3);
+        kstride_bytes = (int)(2 * (MODE == LD_KC ? 1 : sk));
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int b = wave + NW * j;
+            int row, k;
+            if (MODE == LD_KC) KT::src(b, lane, row, k);
+            else RT::src(b, lane, k, row);
+            const bool ok = row < rows_valid;
+            const int64_t e = MODE == LD_KC ? (int64_t)row * srow + k : (int64_t)k * sk + row;
+            voff[j] = ok ? (int)(2 * e) : kOobOffset;
+        }
+    }
+
+    // Queue the tile of k-slice [k0, k0 + BK) into `tile` (this wave's share).
+    __device__ __forceinline__ void issue(char *tile, int k0, int K, int wave, int lane) const {
+        const bool tail = k0 + BK > K;
+        const int soff = k0 * kstride_bytes;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int b = wave + NW * j;
+            int vo = voff[j];
+            if (tail) {
+                int row, k;
+                if (MODE == LD_KC) KT::src(b, lane, row, k);
+                else RT::src(b, lane, k, row);
+                if (k0 + k >= K) vo = kOobOffset;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(tile + b * 1024), 16, vo, soff, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ u32x4 frag(const char *tile, int r0, int k0, int lane) const {
+        if constexpr (MODE == LD_KC) return frag_from_ktile<ROWS, BK>(tile, r0, k0, lane);
+        else return frag_from_rtile<ROWS, BK>(tile, r0, k0, lane);
+    }
+};
+
+template <typename TO, int WTM, int WTN, int FM, int FN>
+__device__ __forceinline__ void store_acc(const GemmArgs &g, const f32x16 (&acc)[FM][FN], int row_base,
+                                          int col_base, bool interior) {
+    typename TO::storage *C = static_cast<typename TO::storage *>(g.C);
+    if (interior) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int64_t cbase = (int64_t)(col_base + j * 32) * g.scn;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    C[(int64_t)gm * g.scm + cbase] = from_f32<TO>(acc[i][j][r]);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int gn = col_base + j * 32;
+                if (gn >= g.N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    if (gm < g.M) C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(acc[i][j][r]);
+                }
+            }
+    }
+}
+
+// WM x WN waves; LA/LB are LD_KC or LD_RC. The host guarantees chunk-exact
+// validity: for an LD_KC operand K % 8 == 0, for an LD_RC operand its row
+// count (M or N) % 8 == 0, and all byte offsets fit in 31 bits.
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+
+    int pm, pn;
+    tile_coords(blockIdx.x, g.grid_m, g.grid_n, g.group_m, g.xcd_remap, g.num_xcd, pm, pn);
+    const int m0 = pm * BM, n0 = pn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    DirectLoader<BM, BK, LA, NW> la;
+    DirectLoader<BN, BK, LB, NW> lb;
+    la.init(static_cast<const uint16_t *>(g.A) + (int64_t)m0 * g.sam, g.sam, g.sak, min(BM, g.M - m0), wave, lane);
+    lb.init(static_cast<const uint16_t *>(g.B) + (int64_t)n0 * g.sbn, g.sbn, g.sbk, min(BN, g.N - n0), wave, lane);
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = (g.K + BK - 1) / BK;
+    if (nk > 0) {
+        la.issue(lds, 0, g.K, wave, lane);
+        lb.issue(lds + A_BYTES, 0, g.K, wave, lane);
+        wait_vmcnt0();
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) {
+            char *nxt = lds + (cur ^ 1) * STAGE;
+            la.issue(nxt, (kt + 1) * BK, g.K, wave, lane);
+            lb.issue(nxt + A_BYTES, (kt + 1) * BK, g.K, wave, lane);
+        }
+        const char *sa = lds + cur * STAGE;
+        const char *sb = sa + A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = la.frag(sa, wm * WTM + i * 32, kk * 16, lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = lb.frag(sb, wn * WTN + j * 32, kk * 16, lane);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<TI>::run(af[i], bf[j], acc[i][j]);
+        }
+        wait_vmcnt0();
+        __syncthreads();
+    }
+
+    const int row_base = m0 + wm * WTM + 4 * (lane >> 5);
+    const int col_base = n0 + wn * WTN + (lane & 31);
+    const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
+    if (g.out_dtype == DG_BF16) store_acc<BF16, WTM, WTN, FM, FN>(g, acc, row_base, col_base, interior);
+    else if (g.out_dtype == DG_F16) store_acc<F16, WTM, WTN, FM, FN>(g, acc, row_base, col_base, interior);
+    else store_acc<F32, WTM, WTN, FM, FN>(g, acc, row_base, col_base, interior);
+}
+
 }  // namespace dg

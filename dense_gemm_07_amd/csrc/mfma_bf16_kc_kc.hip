@@ -1,0 +1,7 @@
+// MFMA kernel instantiations: bf16 inputs, load modes LD_KC / LD_KC.
+#include "dg_kernels.hpp"
+#define DG_TI BF16
+#define DG_LA LD_KC
+#define DG_LB LD_KC
+#define DG_REGISTER register_mfma_bf16_kc_kc
+#include "mfma_inst.inc"

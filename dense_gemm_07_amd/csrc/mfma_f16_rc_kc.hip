@@ -1,0 +1,7 @@
+// MFMA kernel instantiations: f16 inputs, load modes LD_RC / LD_KC.
+#include "dg_kernels.hpp"
+#define DG_TI F16
+#define DG_LA LD_RC
+#define DG_LB LD_KC
+#define DG_REGISTER register_mfma_f16_rc_kc
+#include "mfma_inst.inc"

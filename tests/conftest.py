@@ -40,6 +40,14 @@ def load_grid_counts():
     return out
 
 
+@pytest.fixture(scope="session", autouse=True)
+def _hip_library_built():
+    """Build the HIP library once if nothing is built yet (no rebuild otherwise)."""
+    from dense_gemm_07_amd.build import LIB, build
+    if not os.path.exists(LIB):
+        build()
+
+
 @pytest.fixture(scope="session")
 def oracle_mod():
     import oracle

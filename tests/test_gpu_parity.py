@@ -150,7 +150,9 @@ def test_tiny_shapes_exact(dtype):
         check_exact(a, b, dtype, "f32", what=f"{dtype} {M}x{N}x{K}")
 
 
-RAGGED = [1, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 255, 257, 300]
+# around tile multiples; the multiples of 8 keep the 16-byte vector paths, the rest
+# take the element-load path
+RAGGED = [1, 8, 15, 16, 17, 24, 31, 33, 40, 63, 64, 65, 72, 127, 129, 136, 200, 255, 257, 264, 300, 520]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -158,7 +160,7 @@ RAGGED = [1, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 255, 257, 300]
 def test_ragged_sweep(dtype, layout):
     rng = np.random.default_rng(zlib.crc32(f"{dtype}{layout}".encode()))
     note(f"ragged sweep {dtype} {layout}")
-    for t in range(24):
+    for t in range(40):
         M, N, K = (int(x) for x in rng.choice(RAGGED, 3))
         a, b = inputs.random_operands(M, N, K, dtype, seed=t, dist=("normal", 1.0),
                                       a_colmajor=layout[0] == "t", b_colmajor=layout[1] == "t")
@@ -171,7 +173,9 @@ def test_ragged_sweep(dtype, layout):
 @pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt", "misaligned"])
 def test_every_candidate_bit_exact(in_dtype, layout):
-    M, N, K = 300, 200, 150
+    # multiples of 8 that are not multiples of any tile: vector loads with
+    # M/N edges and a K tail
+    M, N, K = 296, 200, 152
     note(f"all candidates {in_dtype} {layout}")
     if layout == "misaligned":
         # leading dimensions that are not multiples of 8 elements and base
