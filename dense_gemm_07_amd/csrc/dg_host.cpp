@@ -150,11 +150,15 @@ std::pair<int, int> mfma_modes(const Problem &p) {
     return {la, lb};
 }
 
+// The element-load MFMA kernel always double-buffers: for a problem that
+// needs it, a config's `stages` is not part of the match.
 const KernelEntry *find_kernel(const dg_config &cfg, const Problem &p) {
     int la = -1, lb = -1;
     if (cfg.variant == DG_VARIANT_MFMA) std::tie(la, lb) = mfma_modes(p);
     for (const auto &e : registry()) {
-        if (!same_kernel(e.cfg, cfg)) continue;
+        dg_config want = cfg;
+        if (la == LD_GN) want.stages = e.cfg.stages;
+        if (!same_kernel(e.cfg, want)) continue;
         if (e.in_dtype != p.in) continue;
         if (e.out_dtype != -1 && e.out_dtype != p.out) continue;
         if (e.load_a != -1 && e.load_a != la) continue;
@@ -239,19 +243,15 @@ dg_config heuristic(const Problem &p, int cus) {
             }
         }
     } else {
-        // Largest tile that still gives at least one tile per CU; else the
-        // smallest tile. Shapes are registered largest first.
+        // The first registered shape (best first) that has a kernel for this
+        // problem's layouts and gives at least one tile per CU; else the
+        // last usable one (the smallest tile).
         for (const auto &s : shapes) {
+            if (!find_kernel(s, p)) continue;
             const int64_t tiles = ((p.M + s.block_m - 1) / s.block_m) * ((p.N + s.block_n - 1) / s.block_n);
-            if (tiles >= cus) {
-                best = s;
-                have = true;
-                break;
-            }
-        }
-        if (!have && !shapes.empty()) {
-            best = shapes.back();
+            best = s;
             have = true;
+            if (tiles >= cus) break;
         }
     }
     if (!have && !shapes.empty()) best = shapes.front();
@@ -599,8 +599,8 @@ dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_co
         std::sort(times.begin(), times.end());
         const float med = times[times.size() / 2];
         if (log_enabled())
-            fprintf(stderr, "[dg] autotune %dx%dx%d w%d g%d xcd%d: %.4f ms\n", c.block_m, c.block_n, c.block_k,
-                    c.waves, c.group_m, c.xcd_remap, med);
+            fprintf(stderr, "[dg] autotune %dx%dx%d w%d s%d g%d xcd%d: %.4f ms\n", c.block_m, c.block_n, c.block_k,
+                    c.waves, c.stages, c.group_m, c.xcd_remap, med);
         if (!have || med < best_t) {
             best = c;
             best_t = med;

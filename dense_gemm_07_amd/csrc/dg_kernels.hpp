@@ -428,12 +428,23 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 
 template <int ROWS, int BK>
 struct KTile {
-    static_assert(BK == 64, "KTile swizzle assumes 128-byte rows");
+    static_assert(BK == 64 || BK == 32, "KTile rows are 128 or 64 bytes");
     static constexpr int CPR = BK / 8;            // 16-byte chunks per row
     static constexpr int RPL = 1024 / (BK * 2);   // rows per 1 KiB wave load
     static constexpr int NLOADS = ROWS / RPL;
     static constexpr int BYTES = ROWS * BK * 2;
-    __device__ static __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+    // Chunk permutation of a row. A ds_read_b128 fragment read touches one
+    // chunk column of 16 (or 8) consecutive rows; the permutation makes those
+    // land in distinct 16-byte bank groups, whether the LDS serves 8 lanes
+    // per 128 bytes or 16 lanes per 256 bytes.
+    //  128-byte rows: rows r..r+7 need distinct chunks, and so do the 8 rows
+    //                 of one parity among r..r+15.
+    //  64-byte rows:  the 4 rows of one parity among r..r+7, and the 4 rows
+    //                 of one residue mod 4 among r..r+15, need distinct chunks.
+    __device__ static __forceinline__ int swz(int row) {
+        if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
+        else return ((row >> 1) ^ (row >> 3)) & 3;
+    }
     // Element (row, k) of the tile that lane `lane` of wave load `b` fetches (k a multiple of 8).
     __device__ static __forceinline__ void src(int b, int lane, int &row, int &k) {
         row = b * RPL + lane / CPR;
@@ -580,10 +591,58 @@ __device__ __forceinline__ void store_acc(const GemmArgs &g, const f32x16 (&acc)
     }
 }
 
-// WM x WN waves; LA/LB are LD_KC or LD_RC. The host guarantees chunk-exact
-// validity: for an LD_KC operand K % 8 == 0, for an LD_RC operand its row
-// count (M or N) % 8 == 0, and all byte offsets fit in 31 bits.
-template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB>
+// s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this
+// wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier of the LDS pipeline. The caller has waited for the loads
+// it needs. The LDS reads of this wave are drained (lgkmcnt(0)), so the stage
+// they read may be refilled once every wave has passed. Unlike
+// __syncthreads() there is no release fence: that would also wait for the
+// younger loads still in flight into other stages. The empty asm statements
+// keep the compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// No instruction may be scheduled across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Instruction-order hints for the scheduler: NM MFMAs, each followed by its
+// share of ND LDS reads and NV global loads, in that order. Without them the
+// compiler pulls every fragment read down to just before its MFMA (fewest
+// live registers) and the MFMA pipe waits on LDS latency.
+template <int NM, int ND, int NV, int T = 0>
+__device__ __forceinline__ void interleave_mfma() {
+    if constexpr (T < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        constexpr int d = (T + 1) * ND / NM - T * ND / NM;
+        if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);  // LDS reads
+        constexpr int v = (T + 1) * NV / NM - T * NV / NM;
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // global loads
+        interleave_mfma<NM, ND, NV, T + 1>();
+    }
+}
+
+// WM x WN waves; LA/LB are LD_KC or LD_RC; S LDS stages. The host guarantees
+// chunk-exact validity: for an LD_KC operand K % 8 == 0, for an LD_RC operand
+// its row count (M or N) % 8 == 0, and all byte offsets fit in 31 bits.
+//
+// Pipeline: slices 0..S-2 are queued before the loop. Step kt waits until its
+// own slice has landed (the S-2 younger slices may still be in flight),
+// synchronises the workgroup (everyone's copy of slice kt is visible and
+// everyone has finished slice kt-1), queues slice kt+S-1 into the buffer slice
+// kt-1 used, then multiplies slice kt. Slices past K are queued as
+// out-of-range loads (zeros into a free buffer) so that every step issues the
+// same number of loads and the wait count stays a constant.
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -591,8 +650,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     constexpr int STAGE = A_BYTES + B_BYTES;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
+    static_assert(S >= 2, "at least two stages");
 
-    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
     int pm, pn;
     tile_coords(blockIdx.x, g.grid_m, g.grid_n, g.group_m, g.xcd_remap, g.num_xcd, pm, pn);
@@ -602,8 +662,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    DirectLoader<BM, BK, LA, NW> la;
-    DirectLoader<BN, BK, LB, NW> lb;
+    using LoaderA = DirectLoader<BM, BK, LA, NW>;
+    using LoaderB = DirectLoader<BN, BK, LB, NW>;
+    constexpr int LOADS_PER_SLICE = LoaderA::PER + LoaderB::PER;  // per wave
+    LoaderA la;
+    LoaderB lb;
     la.init(static_cast<const uint16_t *>(g.A) + (int64_t)m0 * g.sam, g.sam, g.sak, min(BM, g.M - m0), wave, lane);
     lb.init(static_cast<const uint16_t *>(g.B) + (int64_t)n0 * g.sbn, g.sbn, g.sbk, min(BN, g.N - n0), wave, lane);
 
@@ -616,36 +679,81 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = (g.K + BK - 1) / BK;
+    constexpr int KSUB = BK / 16;  // MFMA k-substeps per slice
+    // Fragment registers, double-buffered across k-substeps: set (kk & 1)
+    // holds substep kk while the other set is being filled.
+    u32x4 af[2][FM], bf[2][FN];
+    // Fetch order follows the MFMA order below (B fragments are all used by
+    // the first row of MFMAs, A fragments one row at a time).
+    auto fetch = [&](const char *stage, int kk, int set) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[set][j] = lb.frag(stage + A_BYTES, wn * WTN + j * 32, kk * 16, lane);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[set][i] = la.frag(stage, wm * WTM + i * 32, kk * 16, lane);
+    };
     if (nk > 0) {
-        la.issue(lds, 0, g.K, wave, lane);
-        lb.issue(lds + A_BYTES, 0, g.K, wave, lane);
-        wait_vmcnt0();
-        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s) {
+            la.issue(lds + s * STAGE, s * BK, g.K, wave, lane);
+            lb.issue(lds + s * STAGE + A_BYTES, s * BK, g.K, wave, lane);
+        }
+        wait_vmcnt<(S - 2) * LOADS_PER_SLICE>();
+        stage_barrier();
+        fetch(lds, 0, 0);
     }
+
+    // One K step over slice kt (in stage `cur`), fragments of its substep 0
+    // already in registers:
+    //  - queue slice kt+S-1 into `fill` (the stage slice kt-1 used: every
+    //    wave finished reading it before the previous barrier);
+    //  - for each substep, fetch the next substep's fragments, then issue
+    //    this substep's MFMAs;
+    //  - before the last substep, wait for slice kt+1 (this wave's loads),
+    //    synchronise, and fetch substep 0 of slice kt+1 from `next`, so the
+    //    MFMA pipe stays fed across the barrier.
+    // Slices past K are queued as out-of-range loads (zeros into a free
+    // stage) so every step issues the same number of loads and the wait
+    // count is a constant. `cur` never overlaps `fill`; saying so (restrict)
+    // keeps the compiler from making the reads of `cur` wait for those loads.
+    constexpr int NMFMA = FM * FN;  // MFMAs per substep
+    constexpr int NREAD = FM * (LA == LD_KC ? 1 : 2) + FN * (LB == LD_KC ? 1 : 2);  // LDS reads per fetch
+    auto mfmas = [&](int set, int from, int to) {
+#pragma unroll
+        for (int t = from; t < to; ++t) acc[t / FN][t % FN] = Mfma<TI>::run(af[set][t / FN], bf[set][t % FN], acc[t / FN][t % FN]);
+    };
+    auto step = [&](char *fill, const char *__restrict__ cur, const char *next, int kt) {
+        la.issue(fill, (kt + S - 1) * BK, g.K, wave, lane);
+        lb.issue(fill + A_BYTES, (kt + S - 1) * BK, g.K, wave, lane);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KSUB; ++kk) {
+            fetch(cur, kk + 1, (kk & 1) ^ 1);
+            mfmas(kk & 1, 0, NMFMA);
+        }
+        // last substep: half of its MFMAs cover the wait and the barrier
+        constexpr int LAST = (KSUB - 1) & 1;
+        mfmas(LAST, 0, NMFMA / 2);
+        // the slice's global loads go out with the first substep's MFMAs
+        interleave_mfma<NMFMA, NREAD, LOADS_PER_SLICE>();
+        interleave_mfma<NMFMA * (KSUB - 2), NREAD * (KSUB - 2), 0>();
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA / 2, 0);
+        sched_fence();
+        wait_vmcnt<(S - 2) * LOADS_PER_SLICE>();
+        stage_barrier();
+        sched_fence();
+        fetch(next, 0, LAST ^ 1);
+        mfmas(LAST, NMFMA / 2, NMFMA);
+        interleave_mfma<NMFMA - NMFMA / 2, NREAD, 0>();
+        sched_fence();
+    };
+    static_assert(KSUB % 2 == 0, "substep 0 of every slice uses fragment set 0");
+    int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            char *nxt = lds + (cur ^ 1) * STAGE;
-            la.issue(nxt, (kt + 1) * BK, g.K, wave, lane);
-            lb.issue(nxt + A_BYTES, (kt + 1) * BK, g.K, wave, lane);
-        }
-        const char *sa = lds + cur * STAGE;
-        const char *sb = sa + A_BYTES;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            u32x4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = la.frag(sa, wm * WTM + i * 32, kk * 16, lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = lb.frag(sb, wn * WTN + j * 32, kk * 16, lane);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<TI>::run(af[i], bf[j], acc[i][j]);
-        }
-        wait_vmcnt0();
-        __syncthreads();
+        const int fill = cur == 0 ? S - 1 : cur - 1;  // stage of slice kt-1 == slice kt+S-1
+        const int next = cur + 1 == S ? 0 : cur + 1;
+        step(lds + fill * STAGE, lds + cur * STAGE, lds + next * STAGE, kt);
+        cur = next;
     }
+    wait_vmcnt<0>();  // the out-of-range tail loads must land before the workgroup can exit
 
     const int row_base = m0 + wm * WTM + 4 * (lane >> 5);
     const int col_base = n0 + wn * WTN + (lane & 31);

@@ -3,5 +3,6 @@
 #define DG_TI BF16
 #define DG_LA LD_GN
 #define DG_LB LD_GN
+#define DG_ELEMENT_LOADS 1
 #define DG_REGISTER register_mfma_bf16_gn
 #include "mfma_inst.inc"

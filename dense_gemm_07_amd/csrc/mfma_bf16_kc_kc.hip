@@ -3,5 +3,6 @@
 #define DG_TI BF16
 #define DG_LA LD_KC
 #define DG_LB LD_KC
+#define DG_ELEMENT_LOADS 0
 #define DG_REGISTER register_mfma_bf16_kc_kc
 #include "mfma_inst.inc"

@@ -3,5 +3,6 @@
 #define DG_TI BF16
 #define DG_LA LD_RC
 #define DG_LB LD_KC
+#define DG_ELEMENT_LOADS 0
 #define DG_REGISTER register_mfma_bf16_rc_kc
 #include "mfma_inst.inc"

@@ -79,7 +79,10 @@ enum {
  *             1 gives plain row-major tile order.
  *  waves:     64-lane wavefronts per workgroup (the num_warps analogue).
  *  stages:    LDS buffers in the K pipeline (num_stages analogue; 2 = load
- *             slice s+1 while slice s is multiplied).
+ *             slice s+1 while slice s is multiplied, S = keep S-1 slices in
+ *             flight). Operands that need element-wise loads (unaligned or
+ *             non-unit-stride layouts) always run a two-buffer pipeline;
+ *             for them the value is not used.
  *  variant:   DG_VARIANT_*.
  *  xcd_remap: 1 = reorder workgroup ids so the tiles dispatched to one XCD
  *             (one L2) are consecutive in the group-major order.
