@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--workload", default="square_4096_bf16")
     ap.add_argument("--no-autotune", action="store_true", help="time the heuristic config instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the GEMM, run torch's device copy of a MIB-sized buffer --steps times "
+                         "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -98,6 +101,15 @@ def main():
     from dense_gemm_07_amd import inputs
     from dense_gemm_07_amd.build import LIB, build
 
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": args.steps}), flush=True)
+        return
     if not os.path.exists(LIB):
         build()
     w = inputs.WORKLOADS[args.workload]

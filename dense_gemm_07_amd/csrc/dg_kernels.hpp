@@ -412,8 +412,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
 //        row-major B). Fragments come from ds_read_b64_tr_b16, which
 //        transposes within 16-lane groups: lane j of a group receives element
 //        (j % 4) of the 4-element rows addressed by lanes 4e + j/4, e = 0..3.
-//        Chunks are XOR-swizzled by 2*(k % 4), so the four k-lines a group
-//        reads fall on distinct banks.
+//        Chunks are XOR-swizzled per k-line so the k-lines a fragment read
+//        touches fall on distinct banks.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -434,16 +434,13 @@ struct KTile {
     static constexpr int NLOADS = ROWS / RPL;
     static constexpr int BYTES = ROWS * BK * 2;
     // Chunk permutation of a row. A ds_read_b128 fragment read touches one
-    // chunk column of 16 (or 8) consecutive rows; the permutation makes those
-    // land in distinct 16-byte bank groups, whether the LDS serves 8 lanes
-    // per 128 bytes or 16 lanes per 256 bytes.
-    //  128-byte rows: rows r..r+7 need distinct chunks, and so do the 8 rows
-    //                 of one parity among r..r+15.
-    //  64-byte rows:  the 4 rows of one parity among r..r+7, and the 4 rows
-    //                 of one residue mod 4 among r..r+15, need distinct chunks.
+    // chunk column of 32 consecutive rows. These permutations were checked
+    // on gfx950 with the LDS bank-conflict counter: both give 4 LDS cycles
+    // per ds_read_b128 (1 KiB), i.e. no conflict cycles. (For 64-byte rows
+    // the permutation ((row >> 1) ^ (row >> 3)) & 3 measured 8 cycles.)
     __device__ static __forceinline__ int swz(int row) {
         if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
-        else return ((row >> 1) ^ (row >> 3)) & 3;
+        else return (row >> 2) & 3;
     }
     // Element (row, k) of the tile that lane `lane` of wave load `b` fetches (k a multiple of 8).
     __device__ static __forceinline__ void src(int b, int lane, int &row, int &k) {
@@ -464,7 +461,17 @@ struct RTile {
     static_assert(KPL >= 1, "RTile k-line larger than one wave load");
     static constexpr int NLOADS = BK / KPL;
     static constexpr int BYTES = ROWS * BK * 2;
-    __device__ static __forceinline__ int swz(int k) { return 2 * (k & 3); }
+    // A ds_read_b64_tr_b16 fragment read touches 4 consecutive k-lines, 64
+    // bytes of each (two 16-lane groups). The permutation moves those 64-byte
+    // pieces to distinct 64-byte bank windows: XOR of the chunk index with
+    // 4*(k % 4) (k-lines of 256 or 512 bytes), or with 4*((k / 2) % 2)
+    // (128-byte k-lines, where k and k+1 already differ by 128 bytes).
+    // Measured on gfx950: 2 LDS cycles per 512-byte tr read, no conflict
+    // cycles; XOR with 2*(k % 4) measured 4 cycles.
+    __device__ static __forceinline__ int swz(int k) {
+        if constexpr (CPR >= 16) return 4 * (k & 3);
+        else return 4 * ((k >> 1) & 1);
+    }
     __device__ static __forceinline__ void src(int b, int lane, int &k, int &row) {
         k = b * KPL + lane / CPR;
         row = ((lane % CPR) ^ swz(k)) * 8;
