@@ -23,7 +23,7 @@ HBM_GBPS = 8000.0
 METRIC = "TFLOP/s and % of MFMA dense peak, 4096³ bf16 GEMM on 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["dense_gemm_07_amd/csrc/dg_kernels.hpp", "dense_gemm_07_amd/csrc/dg_internal.hpp",
-                  "dense_gemm_07_amd/csrc/mfma_inst.inc"]
+                  "dense_gemm_07_amd/csrc/mfma_units.hpp"]
 
 
 def kernel_source_hash():

@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["dg_host.cpp", "simt.hip"] + [
-    f"mfma_{t}_{m}.hip" for t in ("bf16", "f16") for m in ("kc_rc", "kc_kc", "rc_rc", "rc_kc", "gn")]
+    f"mfma_{t}_{m}.hip" for t in ("bf16", "f16") for m in ("kc_rc", "kc_kc", "rc_rc", "rc_kc", "gn", "unaligned")]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

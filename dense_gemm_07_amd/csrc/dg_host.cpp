@@ -125,11 +125,13 @@ const std::vector<KernelEntry> &registry() {
         register_mfma_bf16_rc_rc(r);
         register_mfma_bf16_rc_kc(r);
         register_mfma_bf16_gn(r);
+        register_mfma_bf16_unaligned(r);
         register_mfma_f16_kc_rc(r);
         register_mfma_f16_kc_kc(r);
         register_mfma_f16_rc_rc(r);
         register_mfma_f16_rc_kc(r);
         register_mfma_f16_gn(r);
+        register_mfma_f16_unaligned(r);
         return r;
     }();
     return reg;
@@ -140,24 +142,38 @@ bool same_kernel(const dg_config &a, const dg_config &b) {
            a.stages == b.stages && a.variant == b.variant;
 }
 
-// Effective load modes of the MFMA kernels for a problem: the four vector
-// combinations are compiled; anything with an element-load operand uses the
-// element-load kernel for both.
-std::pair<int, int> mfma_modes(const Problem &p) {
-    int la = load_mode(p.A, p.M, p.K, p.sam, p.sak);
-    int lb = load_mode(p.B, p.N, p.K, p.sbn, p.sbk);
-    if (la == LD_GN || lb == LD_GN) la = lb = LD_GN;
-    return {la, lb};
+// Register-staged load mode of an operand (rows x K, strides srow, sk):
+// contiguous along k or along rows at any element alignment, else elements.
+int staged_mode(int64_t rows, int64_t K, int64_t srow, int64_t sk) {
+    if (sk == 1 || K <= 1) return LD_KU;
+    if (srow == 1 || rows <= 1) return LD_RU;
+    return LD_GN;
 }
 
-// The element-load MFMA kernel always double-buffers: for a problem that
+// Effective load modes of the MFMA kernels for a problem. Both operands in a
+// 16-byte vector layout: the direct-to-LDS kernel. Otherwise the
+// register-staged kernel: contiguous operands keep 16-byte loads at any
+// alignment; an operand with no unit stride makes both use element loads.
+std::pair<int, int> mfma_modes(const Problem &p) {
+    const int la = load_mode(p.A, p.M, p.K, p.sam, p.sak);
+    const int lb = load_mode(p.B, p.N, p.K, p.sbn, p.sbk);
+    if (la != LD_GN && lb != LD_GN) return {la, lb};
+    const int sa = staged_mode(p.M, p.K, p.sam, p.sak);
+    const int sb = staged_mode(p.N, p.K, p.sbn, p.sbk);
+    if (sa == LD_GN || sb == LD_GN) return {LD_GN, LD_GN};
+    return {sa, sb};
+}
+
+bool register_staged(int la) { return la == LD_KU || la == LD_RU || la == LD_GN; }
+
+// The register-staged MFMA kernel always double-buffers: for a problem that
 // needs it, a config's `stages` is not part of the match.
 const KernelEntry *find_kernel(const dg_config &cfg, const Problem &p) {
     int la = -1, lb = -1;
     if (cfg.variant == DG_VARIANT_MFMA) std::tie(la, lb) = mfma_modes(p);
     for (const auto &e : registry()) {
         dg_config want = cfg;
-        if (la == LD_GN) want.stages = e.cfg.stages;
+        if (cfg.variant == DG_VARIANT_MFMA && register_staged(la)) want.stages = e.cfg.stages;
         if (!same_kernel(e.cfg, want)) continue;
         if (e.in_dtype != p.in) continue;
         if (e.out_dtype != -1 && e.out_dtype != p.out) continue;

@@ -29,10 +29,14 @@ struct GemmArgs {
 
 // How an operand tile is fetched from global memory. The operand is viewed
 // as rows x K (rows = M for A, N for B) with a row stride and a k stride.
+// LD_KC / LD_RC select the direct-to-LDS kernel; LD_KU / LD_RU / LD_GN the
+// register-staged kernel.
 enum LoadMode : int32_t {
     LD_KC = 0,  // k-contiguous (k stride 1), 16-byte aligned rows, K % 8 == 0
     LD_RC = 1,  // row-contiguous (row stride 1), 16-byte aligned k-lines, rows % 8 == 0
     LD_GN = 2,  // anything else: element loads through both strides
+    LD_KU = 3,  // k-contiguous, any element alignment
+    LD_RU = 4,  // row-contiguous, any element alignment
 };
 
 using LaunchFn = hipError_t (*)(const GemmArgs &, hipStream_t);
@@ -55,7 +59,8 @@ void register_simt(std::vector<KernelEntry> &out);
     void register_mfma_##t##_kc_kc(std::vector<KernelEntry> &out); \
     void register_mfma_##t##_rc_rc(std::vector<KernelEntry> &out); \
     void register_mfma_##t##_rc_kc(std::vector<KernelEntry> &out); \
-    void register_mfma_##t##_gn(std::vector<KernelEntry> &out);
+    void register_mfma_##t##_gn(std::vector<KernelEntry> &out);    \
+    void register_mfma_##t##_unaligned(std::vector<KernelEntry> &out);
 DG_DECLARE_MFMA_HOOKS(bf16)
 DG_DECLARE_MFMA_HOOKS(f16)
 #undef DG_DECLARE_MFMA_HOOKS

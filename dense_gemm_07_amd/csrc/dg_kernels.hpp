@@ -174,18 +174,34 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     }
 }
 
+// 16 bytes from an address that is only element (2-byte) aligned. gfx950
+// serves unaligned global vector loads; the compiler emits one
+// global_load_dwordx4 for this.
+typedef unsigned int u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+__device__ __forceinline__ u32x4 load16_unaligned(const uint16_t *p) {
+    const u32x4_a2 v = *reinterpret_cast<const u32x4_a2 *>(p);
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+
 // Fetches one operand tile (ROWS x BK, rows = M for A or N for B) from
 // global memory into registers, then writes it to LDS as [ROWS][LDK] with k
 // contiguous. Elements outside the operand's view (row >= rows_valid or
 // k >= K) become +0 and are never read.
+//  LD_KU: k stride 1. Whole 8-element chunks are one 16-byte load at any
+//         element alignment; a chunk cut by K is loaded element by element.
+//  LD_RU: row stride 1. 8x8 blocks: eight 16-byte loads along the rows, then
+//         an in-register transpose; a block cut by the row count is loaded
+//         element by element.
+//  LD_GN: anything else, element loads through both strides.
 template <int ROWS, int BK, int LDK, int T, int MODE>
 struct TileLoader {
+    static_assert(MODE == LD_KU || MODE == LD_RU || MODE == LD_GN, "register-staged load modes");
     static constexpr int KCH = BK / 8;                   // 8-element k-chunks per row
-    static constexpr int NCH = ROWS * KCH;               // chunks per tile (KC, GN)
+    static constexpr int NCH = ROWS * KCH;               // chunks per tile (KU, GN)
     static constexpr int PER = (NCH + T - 1) / T;
-    static constexpr int NBL = (ROWS / 8) * KCH;         // 8x8 blocks per tile (RC)
+    static constexpr int NBL = (ROWS / 8) * KCH;         // 8x8 blocks per tile (RU)
     static constexpr int PERB = (NBL + T - 1) / T;
-    static constexpr int NREG = MODE == LD_RC ? PERB * 8 : PER;
+    static constexpr int NREG = MODE == LD_RU ? PERB * 8 : PER;
 
     u32x4 reg[NREG];
     const uint16_t *base;  // element (row0, k = 0) of the operand
@@ -194,7 +210,7 @@ struct TileLoader {
     int K;
 
     __device__ __forceinline__ void load(int tid, int k0) {
-        if constexpr (MODE == LD_RC) {
+        if constexpr (MODE == LD_RU) {
 #pragma unroll
             for (int b = 0; b < PERB; ++b) {
                 const int q = b * T + tid;
@@ -209,7 +225,7 @@ struct TileLoader {
                     if (qok && k < K) {
                         const uint16_t *p = base + (int64_t)k * sk + r0;
                         if (r0 + 8 <= rows_valid) {
-                            v = *reinterpret_cast<const u32x4 *>(p);
+                            v = load16_unaligned(p);
                         } else if (r0 < rows_valid) {
                             uint16_t e8[8];
 #pragma unroll
@@ -232,10 +248,10 @@ struct TileLoader {
                 const int k = k0 + kc * 8;
                 const bool ok = ((NCH % T == 0) || q < NCH) && r < rows_valid;
                 u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                if (MODE == LD_KC) {
+                if (MODE == LD_KU) {
                     const uint16_t *p = base + (int64_t)r * srow + k;
                     if (ok && k + 8 <= K) {
-                        v = *reinterpret_cast<const u32x4 *>(p);
+                        v = load16_unaligned(p);
                     } else if (ok && k < K) {
                         uint16_t e8[8];
 #pragma unroll
@@ -257,7 +273,7 @@ struct TileLoader {
     }
 
     __device__ __forceinline__ void store(int tid, uint16_t *lds) const {
-        if constexpr (MODE == LD_RC) {
+        if constexpr (MODE == LD_RU) {
 #pragma unroll
             for (int b = 0; b < PERB; ++b) {
                 const int q = b * T + tid;

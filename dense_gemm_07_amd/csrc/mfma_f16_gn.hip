@@ -1,8 +1,7 @@
-// MFMA kernel instantiations: f16 inputs, load modes LD_GN / LD_GN.
-#include "dg_kernels.hpp"
-#define DG_TI F16
-#define DG_LA LD_GN
-#define DG_LB LD_GN
-#define DG_ELEMENT_LOADS 1
-#define DG_REGISTER register_mfma_f16_gn
-#include "mfma_inst.inc"
+// MFMA kernel instantiations: f16 inputs.
+#include "mfma_units.hpp"
+namespace dg {
+void register_mfma_f16_gn(std::vector<KernelEntry> &out) {
+    add_shapes<F16, LD_GN, LD_GN>(out);
+}
+}  // namespace dg

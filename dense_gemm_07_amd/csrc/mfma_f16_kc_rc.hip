@@ -1,8 +1,7 @@
-// MFMA kernel instantiations: f16 inputs, load modes LD_KC / LD_RC.
-#include "dg_kernels.hpp"
-#define DG_TI F16
-#define DG_LA LD_KC
-#define DG_LB LD_RC
-#define DG_ELEMENT_LOADS 0
-#define DG_REGISTER register_mfma_f16_kc_rc
-#include "mfma_inst.inc"
+// MFMA kernel instantiations: f16 inputs.
+#include "mfma_units.hpp"
+namespace dg {
+void register_mfma_f16_kc_rc(std::vector<KernelEntry> &out) {
+    add_shapes<F16, LD_KC, LD_RC>(out);
+}
+}  // namespace dg

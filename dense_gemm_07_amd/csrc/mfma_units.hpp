@@ -1,0 +1,53 @@
+// Registration helpers shared by the MFMA instantiation units.
+#pragma once
+
+#include <vector>
+
+#include "dg_kernels.hpp"
+
+namespace dg {
+
+template <int LA, int LB>
+constexpr bool direct_to_lds() {
+    return (LA == LD_KC || LA == LD_RC) && (LB == LD_KC || LB == LD_RC);
+}
+
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
+hipError_t launch_mfma(const GemmArgs &g, hipStream_t s) {
+    const unsigned tiles = (unsigned)g.grid_m * (unsigned)g.grid_n;
+    if constexpr (direct_to_lds<LA, LB>())
+        hipLaunchKernelGGL((gemm_mfma_lds<TI, BM, BN, BK, WM, WN, LA, LB, S>), dim3(tiles), dim3(WM * WN * 64), 0,
+                           s, g);
+    else
+        hipLaunchKernelGGL((gemm_mfma<TI, BM, BN, BK, WM, WN, LA, LB>), dim3(tiles), dim3(WM * WN * 64), 0, s, g);
+    return hipGetLastError();
+}
+
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
+void add_mfma(std::vector<KernelEntry> &out) {
+    out.push_back(KernelEntry{dg_config{BM, BN, BK, 1, WM * WN, S, DG_VARIANT_MFMA, 0}, TI::code, -1, LA, LB,
+                              &launch_mfma<TI, BM, BN, BK, WM, WN, LA, LB, S>,
+                              direct_to_lds<LA, LB>() ? "gemm_mfma_lds" : "gemm_mfma"});
+}
+
+// Every tile shape has a two-stage kernel for every load-mode pair (the
+// register-staged kernel is two-stage only); the direct-to-LDS kernel adds
+// deeper pipelines. Order matters: the heuristic takes the first shape that
+// fills the GPU.
+template <typename TI, int LA, int LB>
+void add_shapes(std::vector<KernelEntry> &out) {
+    constexpr bool direct = direct_to_lds<LA, LB>();
+    if constexpr (direct) {
+        add_mfma<TI, 256, 256, 32, 2, 4, LA, LB, 3>(out);
+        add_mfma<TI, 256, 256, 32, 2, 4, LA, LB, 4>(out);
+    }
+    add_mfma<TI, 256, 256, 64, 2, 4, LA, LB, 2>(out);
+    add_mfma<TI, 256, 256, 32, 2, 4, LA, LB, 2>(out);
+    add_mfma<TI, 256, 128, 64, 2, 2, LA, LB, 2>(out);
+    add_mfma<TI, 128, 256, 64, 2, 2, LA, LB, 2>(out);
+    if constexpr (direct) add_mfma<TI, 128, 128, 64, 2, 2, LA, LB, 3>(out);
+    add_mfma<TI, 128, 128, 64, 2, 2, LA, LB, 2>(out);
+    add_mfma<TI, 64, 64, 64, 2, 2, LA, LB, 2>(out);
+}
+
+}  // namespace dg

@@ -284,3 +284,18 @@ def test_invalid_arguments_launch_nothing():
     assert e.value.status == 3
     torch.cuda.synchronize()
     assert torch.all(c.cpu() == 7.0)
+
+
+@pytest.mark.parametrize("in_dtype", ["f16", "bf16"])
+def test_no_unit_stride_operands(in_dtype):
+    """Views with no unit stride on either axis take the element-load path."""
+    M, N, K = 150, 90, 70
+    big_a, big_b = inputs.integer_operands(2 * M, 2 * N, 2 * K, in_dtype, seed=61)
+    a_cpu, b_cpu = big_a[::2, ::2], big_b[::2, ::2]          # strides (2*2K, 2), (2*2N, 2)
+    a = big_a.to(DEV)[::2, ::2]
+    b = big_b.to(DEV)[::2, ::2]
+    for out in ("f32", "bf16"):
+        want = oracle.encode(ref_full(a_cpu, b_cpu, in_dtype), out)
+        c = dg.gemm(a, b, out_dtype=TD[out])
+        torch.cuda.synchronize()
+        assert_bits_equal(out_bits(c, out), want, f"strided {in_dtype} -> {out}")
