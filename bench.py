@@ -1,10 +1,10 @@
 """Benchmark: TFLOP/s and fraction of the MFMA dense peak of C = A @ B on one MI355X.
 
 One step is one product over the workload's synthetic operands (seeded, see
-dense_gemm_07_amd/inputs.py), inputs already resident in HBM. The config is
-autotuned once before timing (a one-time cost, reported separately); the timed
-steps call the library's normal gemm entry point, which uses the cached
-winner. Prints one JSON line.
+dense_gemm_07_amd/inputs.py), inputs already resident in HBM. The timed steps
+call the library's normal gemm entry point with its built-in config choice;
+--autotune first benchmarks the candidates and times the cached winner (a
+one-time cost, reported separately). Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -47,6 +47,46 @@ def measured_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_median(csv_path, counter, kernel_substr=None):
+    """Median value of one rocprofv3 counter over the dispatches of one kernel:
+    the kernel whose name contains kernel_substr, or, if None, the kernel
+    dispatched most often in the run."""
+    import csv
+    import statistics
+    groups = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and (kernel_substr is None or kernel_substr in r["Kernel_Name"]):
+            groups.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    if not groups:
+        raise SystemExit(f"no {counter} samples for {kernel_substr!r} in {csv_path}")
+    vals = [v for g in groups.values() for v in g] if kernel_substr else max(groups.values(), key=len)
+    return statistics.median(vals), sorted(groups) if kernel_substr else [max(groups, key=lambda k: len(groups[k]))]
+
+
+def record_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, commands):
+    """HBM bytes per GEMM launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a device copy of
+    copy_mib MiB; written to profiles/traffic_<workload>.json with the hash of
+    the kernel sources it was taken on."""
+    fetch, kernels = _counter_median(fetch_csv, "FETCH_SIZE", "dg::gemm")
+    write, _ = _counter_median(write_csv, "WRITE_SIZE", "dg::gemm")
+    copy_kib = copy_mib * 1024.0
+    cf, _ = _counter_median(copy_fetch_csv, "FETCH_SIZE")
+    cw, _ = _counter_median(copy_write_csv, "WRITE_SIZE")
+    fs, ws = copy_kib / cf, copy_kib / cw
+    rec = {"workload": workload, "kernels": kernels, "kernel_source_hash": kernel_source_hash(),
+           "fetch_size_kib_raw": fetch, "write_size_kib_raw": write,
+           "copy_calibration_mib": copy_mib, "copy_fetch_size_kib_raw": cf, "copy_write_size_kib_raw": cw,
+           "fetch_scale": fs, "write_scale": ws,
+           "hbm_read_bytes_per_launch": round(fetch * fs * 1024), "hbm_write_bytes_per_launch": round(write * ws * 1024),
+           "hbm_bytes_per_launch": round((fetch * fs + write * ws) * 1024), "commands": commands}
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def cpu_baseline(w, a_cpu, b_cpu, target_s=10.0):
     """The oracle, as it stands, on a row slice of the same product."""
     import oracle
@@ -84,12 +124,20 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square_4096_bf16")
-    ap.add_argument("--no-autotune", action="store_true", help="time the heuristic config instead")
+    ap.add_argument("--autotune", action="store_true", help="autotune first and time the winner")
+    ap.add_argument("--no-autotune", action="store_true", help="(default) time the built-in config choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run torch's device copy of a MIB-sized buffer --steps times "
                          "(reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="no GPU work: turn rocprofv3 counter CSVs into profiles/traffic_<workload>.json")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (with --record-traffic)")
+    ap.add_argument("--commands", default="", help="commands that produced the CSVs (with --record-traffic)")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic, args.copy_mib, args.commands)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
               f"(the product shards without exchange, but no multi-GPU path is built).", file=sys.stderr)
@@ -112,7 +160,7 @@ def main():
         return
     if not os.path.exists(LIB):
         build()
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.WORKLOADS.get(args.workload) or inputs.SKINNY[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     a_cpu, b_cpu = inputs.make(w, seed=0)
@@ -122,7 +170,7 @@ def main():
     torch.cuda.synchronize()
 
     tune_s = 0.0
-    if not args.no_autotune:
+    if args.autotune and not args.no_autotune:
         t0 = time.perf_counter()
         cfg, _ = dg.autotune(a, b, out=c, repeats=10)
         tune_s = time.perf_counter() - t0
@@ -145,6 +193,14 @@ def main():
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.in_dtype]
     traffic = measured_traffic(w.name)
+    hbm_bound = w.flops / w.compulsory_bytes() < peak * 1e12 / (HBM_GBPS * 1e9)
+    if hbm_bound:  # below the ridge: algorithmic bytes over time against the HBM peak
+        gbps = w.compulsory_bytes() / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / HBM_GBPS, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4), "traffic": traffic}
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -162,8 +218,7 @@ def main():
                    "name": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "b_layout": "col-major" if w.b_colmajor else "row-major",
                    "kernel_config": cfg.as_dict(), "autotune_s": round(tune_s, 3)},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, a_cpu, b_cpu)

@@ -261,13 +261,21 @@ dg_config heuristic(const Problem &p, int cus) {
     } else {
         // The first registered shape (best first) that has a kernel for this
         // problem's layouts and gives at least one tile per CU; else the
-        // last usable one (the smallest tile).
+        // first usable shape with the most tiles.
+        int64_t most = -1;
         for (const auto &s : shapes) {
             if (!find_kernel(s, p)) continue;
             const int64_t tiles = ((p.M + s.block_m - 1) / s.block_m) * ((p.N + s.block_n - 1) / s.block_n);
-            best = s;
-            have = true;
-            if (tiles >= cus) break;
+            if (tiles >= cus) {
+                best = s;
+                have = true;
+                break;
+            }
+            if (tiles > most) {
+                most = tiles;
+                best = s;
+                have = true;
+            }
         }
     }
     if (!have && !shapes.empty()) best = shapes.front();

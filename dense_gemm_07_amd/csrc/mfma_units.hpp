@@ -37,17 +37,26 @@ void add_mfma(std::vector<KernelEntry> &out) {
 template <typename TI, int LA, int LB>
 void add_shapes(std::vector<KernelEntry> &out) {
     constexpr bool direct = direct_to_lds<LA, LB>();
+    add_mfma<TI, 256, 256, 64, 2, 4, LA, LB, 2>(out);
     if constexpr (direct) {
         add_mfma<TI, 256, 256, 32, 2, 4, LA, LB, 3>(out);
         add_mfma<TI, 256, 256, 32, 2, 4, LA, LB, 4>(out);
     }
-    add_mfma<TI, 256, 256, 64, 2, 4, LA, LB, 2>(out);
     add_mfma<TI, 256, 256, 32, 2, 4, LA, LB, 2>(out);
     add_mfma<TI, 256, 128, 64, 2, 2, LA, LB, 2>(out);
     add_mfma<TI, 128, 256, 64, 2, 2, LA, LB, 2>(out);
-    if constexpr (direct) add_mfma<TI, 128, 128, 64, 2, 2, LA, LB, 3>(out);
+    if constexpr (direct) {
+        add_mfma<TI, 128, 128, 64, 2, 2, LA, LB, 3>(out);
+        add_mfma<TI, 128, 128, 64, 2, 2, LA, LB, 4>(out);
+    }
     add_mfma<TI, 128, 128, 64, 2, 2, LA, LB, 2>(out);
+    // small tiles: short K loops are latency-bound, so keep more slices in flight
+    if constexpr (direct) {
+        add_mfma<TI, 64, 64, 64, 2, 2, LA, LB, 4>(out);
+        add_mfma<TI, 64, 64, 32, 2, 2, LA, LB, 8>(out);
+    }
     add_mfma<TI, 64, 64, 64, 2, 2, LA, LB, 2>(out);
+    add_mfma<TI, 64, 64, 32, 2, 2, LA, LB, 2>(out);
 }
 
 }  // namespace dg

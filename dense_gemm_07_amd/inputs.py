@@ -57,6 +57,16 @@ WORKLOADS = {
 }
 
 
+# Skinny products (few rows of A against the MLP weight shape): bandwidth-bound,
+# measured in HBM GB/s. Not among the five workloads above.
+SKINNY = {
+    w.name: w for w in [
+        Workload(f"skinny_m{m}_14336x4096_bf16", m, 14336, 4096, "bf16", "bf16", ("normal", 1.0), ("normal", 0.02))
+        for m in (1, 16, 64, 128)
+    ]
+}
+
+
 def _draw(shape, dist, gen):
     if dist[0] == "uniform":
         return torch.rand(shape, generator=gen, dtype=torch.float32) * 2.0 - 1.0

@@ -86,8 +86,32 @@ def test_workload_random_full(name):
 
 
 @pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_default_launch(name):
+    """The launch configuration the benchmark times: gemm with the built-in
+    config choice, at full size, sampled against the oracle."""
+    w = inputs.WORKLOADS[name]
+    note(f"workload {name} (default config, sampled oracle)")
+    a_cpu, b_cpu = inputs.make(w)
+    a = inputs.to_device_like(a_cpu, DEV)
+    b = inputs.to_device_like(b_cpu, DEV)
+    c = torch.full((w.M, w.N), float("nan"), dtype=TD[w.out_dtype], device=DEV)
+    dg.cache_clear()
+    cfg, hit = dg.select_config(a, b, c)
+    assert not hit
+    dg.gemm(a, b, out=c)
+    torch.cuda.synchronize()
+    note(f"  config {cfg}")
+    rows, cols = sample_indices(w.M, w.N, 3000, seed=4)
+    ref = oracle.gemm_entries(inputs.bits(a_cpu, w.in_dtype), inputs.bits(b_cpu, w.in_dtype), w.in_dtype,
+                              rows, cols)
+    got = to_f64(c)
+    assert np.all(np.isfinite(got)), "C not fully written"
+    assert_within(got[rows, cols], ref, w.K, w.in_dtype, w.out_dtype, name)
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
 def test_workload_autotuned_launch(name):
-    """The launch configuration the benchmark times: autotune, then gemm."""
+    """bench.py --autotune: autotune, then gemm with the cached winner."""
     w = inputs.WORKLOADS[name]
     note(f"workload {name} (autotuned config, sampled oracle)")
     a_cpu, b_cpu = inputs.make(w)
