@@ -6,6 +6,7 @@ it. The arithmetic lives in `ref_gemm.c` (plain C, fp64, k-ascending sums);
 `brute.py` is an exact rational cross-check for tiny shapes.
 
 Dtype codes here are the oracle's own: "f32", "f16", "bf16".
+Activation names: "none", "relu", "gelu".
 
 Parity status: every function is pinned (tests/test_oracle.py) against the
 pages' worked examples, closed forms, invariants and an exact brute force.
@@ -36,6 +37,8 @@ def _load():
         lib.ref_gemm.restype = ctypes.c_int
         lib.ref_gemm_entries.argtypes = [i64, ctypes.c_int, p, i64, i64, p, i64, i64, i64, p, p, p]
         lib.ref_gemm_rows.argtypes = [i64, i64, i64, i64, ctypes.c_int, p, i64, i64, p, i64, i64, p]
+        d, c = ctypes.c_double, ctypes.c_int
+        lib.ref_epilogue.argtypes = [i64, i64, p, i64, d, d, c, p, i64, i64, c, p, i64, c, c, p, i64]
         _lib = lib
     return _lib
 
@@ -129,3 +132,41 @@ def gemm_rows(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str,
     _load().ref_gemm_rows(row0, nrows, N, K, _CODES[dtype], pa, sam, sak, pb, sbk, sbn,
                           out.ctypes.data)
     return out
+
+
+_ACTS = {"none": 0, "relu": 1, "gelu": 2}
+
+
+def epilogue(p: np.ndarray, alpha=1.0, beta=0.0, r_bits=None, r_dtype=None,
+             bias_bits=None, bias_dtype=None, per_row=False, act="none") -> np.ndarray:
+    """act(alpha * P + beta * R + bias) in fp64 (ref_epilogue in ref_gemm.c).
+
+    p: [M, N] fp64 product. alpha and beta are rounded to fp32 first (the
+    values a caller of the GPU library can pass). r_bits: [M, N] view of raw
+    bits (read only when beta != 0); bias_bits: 1-D view of raw bits, one per
+    column (per_row False) or per row.
+    """
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    M, N = p.shape
+    alpha, beta = float(np.float32(alpha)), float(np.float32(beta))
+    rp, (srm, srn), rcode = None, (0, 0), 0
+    if beta != 0.0:
+        if r_bits is None or tuple(r_bits.shape) != (M, N):
+            raise ValueError("beta != 0 needs an [M, N] residual")
+        rp, (srm, srn) = _operand(r_bits, r_dtype)
+        rcode = _CODES[r_dtype]
+    bp, sb, bcode = None, 0, 0
+    if bias_bits is not None:
+        if bias_bits.ndim != 1 or bias_bits.shape[0] != (M if per_row else N):
+            raise ValueError("bias length must be M (per_row) or N")
+        bp, (sb,) = _operand(bias_bits, bias_dtype)
+        bcode = _CODES[bias_dtype]
+    out = np.empty((M, N), dtype=np.float64)
+    _load().ref_epilogue(M, N, p.ctypes.data, N, alpha, beta, rcode, rp, srm, srn,
+                         bcode, bp, sb, 1 if per_row else 0, _ACTS[act], out.ctypes.data, N)
+    return out
+
+
+def gemm_ex(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, **epi) -> np.ndarray:
+    """The product followed by the fused epilogue (arguments of `epilogue`)."""
+    return epilogue(gemm(a_bits, b_bits, dtype), **epi)

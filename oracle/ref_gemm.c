@@ -244,3 +244,46 @@ void ref_gemm_rows(int64_t row0, int64_t nrows, int64_t N, int64_t K, int dtype,
             out[r * N + j] = s;
         }
 }
+
+/*
+ * Fused epilogue over a product P already computed above (row-major fp64,
+ * leading dimension ldp):
+ *
+ *   out[i][j] = act(alpha * P[i][j] + beta * R[i][j] + bias)
+ *
+ * The pages name the two uses this serves -- the product standing in for a
+ * linear layer ("如何用Triton手写Kernel优化矩阵乘与Flash Attention？",
+ * 性能对比与工程落地建议) and element-wise steps fused into the kernel that
+ * produces their input ("用 Triton 写 GPU Kernel：从 Vector Add、Softmax 到
+ * MatMul", §2.7) -- but give no formula. Reading taken: the BLAS form
+ * alpha*P + beta*R, plus a bias broadcast along rows (bias[j], per column) or
+ * along columns (bias[i], per row), then an activation, all in fp64 in the
+ * order written, rounded once by the caller.
+ *  - alpha and beta are the fp32 values the caller passes (exact in fp64).
+ *  - beta == 0: R is not read (a NaN in R does not reach the result).
+ *  - R[i][j] at R + i*srm + j*srn, bias at bias + (per_row ? i : j)*sbias,
+ *    decoded exactly like A and B. bias == NULL: no bias.
+ *  - act 0: none. act 1: ReLU, v < 0 -> +0, anything else (NaN, -0) kept.
+ *    act 2: GELU, v * Phi(v) with Phi the standard normal CDF,
+ *    Phi(v) = erfc(-v / sqrt(2)) / 2 (C99 erfc in fp64).
+ */
+static double ref_act(double v, int act) {
+    if (act == 1) return v < 0.0 ? 0.0 : v;
+    if (act == 2) return v * 0.5 * erfc(-v / sqrt(2.0));
+    return v;
+}
+
+void ref_epilogue(int64_t M, int64_t N, const double *P, int64_t ldp,
+                  double alpha, double beta,
+                  int r_dtype, const void *R, int64_t srm, int64_t srn,
+                  int bias_dtype, const void *bias, int64_t sbias, int per_row,
+                  int act, double *out, int64_t ldo) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * P[i * ldp + j];
+            if (beta != 0.0) v += beta * dec_at(r_dtype, R, i * srm + j * srn);
+            if (bias) v += dec_at(bias_dtype, bias, (per_row ? i : j) * sbias);
+            out[i * ldo + j] = ref_act(v, act);
+        }
+}

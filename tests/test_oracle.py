@@ -325,3 +325,112 @@ def test_error_bound_of_fp64_sums(oracle_mod):
             s = float(sum(abs(fa[i][k] * fb[k][j]) for k in range(500)))
             assert abs(Fraction(got[i, j]) - exact[i][j]) <= Fraction(500 * 2.0 ** -53 * s)
             assert math.isfinite(got[i, j])
+
+
+# ---- fused epilogue -----------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_epilogue_hand_2x2(oracle_mod, dtype):
+    g = load_golden("epilogue_2x2_hand.txt")
+    a, b, r = as_bits(g["A"], dtype), as_bits(g["B"], dtype), as_bits(g["R"], dtype)
+    bias = as_bits(g["BIAS"][0], dtype)
+    alpha, beta = g["ALPHA"][0][0], g["BETA"][0][0]
+    for per_row, tag in ((False, "COL"), (True, "ROW")):
+        for act in ("none", "relu"):
+            got = oracle_mod.gemm_ex(a, b, dtype, alpha=alpha, beta=beta, r_bits=r, r_dtype=dtype,
+                                     bias_bits=bias, bias_dtype=dtype, per_row=per_row, act=act)
+            assert got.tolist() == g[f"{tag}_{act.upper()}"], (tag, act)
+
+
+# Standard normal CDF values from printed tables (Phi(x) to 16 digits).
+PHI_TABLE = {
+    -3.0: 0.0013498980316300946,
+    -1.5: 0.0668072012688581,
+    -1.0: 0.15865525393145707,
+    0.5: 0.6914624612740131,
+    1.0: 0.8413447460685429,
+    2.0: 0.9772498680518208,
+}
+
+
+def test_gelu_matches_normal_cdf_table(oracle_mod):
+    xs = np.array([list(PHI_TABLE)], dtype=np.float64)
+    got = oracle_mod.epilogue(xs, act="gelu")[0]
+    want = np.array([x * phi for x, phi in PHI_TABLE.items()])
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+    # GELU(0) = 0 and GELU(x) - GELU(-x) = x (since Phi(x) + Phi(-x) = 1)
+    assert oracle_mod.epilogue(np.zeros((1, 1)), act="gelu")[0, 0] == 0.0
+    x = np.linspace(-6, 6, 97).reshape(1, -1)
+    g = oracle_mod.epilogue(x, act="gelu")
+    gm = oracle_mod.epilogue(-x, act="gelu")
+    assert np.allclose(g - gm, x, rtol=0, atol=1e-14)
+
+
+def test_relu_special_values(oracle_mod):
+    x = np.array([[-1.0, -0.0, 0.0, 2.5, np.nan, -np.inf, np.inf]])
+    got = oracle_mod.epilogue(x, act="relu")[0]
+    assert got[0] == 0.0 and not np.signbit(got[0])
+    assert got[1] == 0.0 and np.signbit(got[1])  # -0 is not < 0: kept
+    assert got[2] == 0.0 and got[3] == 2.5
+    assert np.isnan(got[4]) and got[5] == 0.0 and got[6] == np.inf
+
+
+def test_epilogue_beta_zero_never_reads_residual(oracle_mod):
+    p = np.arange(6, dtype=np.float64).reshape(2, 3)
+    r = np.full((2, 3), np.nan, dtype=np.float32).view(np.uint32)
+    got = oracle_mod.epilogue(p, alpha=1.0, beta=0.0, r_bits=r, r_dtype="f32")
+    assert np.array_equal(got, p)
+    with_beta = oracle_mod.epilogue(p, alpha=1.0, beta=1.0, r_bits=r, r_dtype="f32")
+    assert np.isnan(with_beta).all()
+
+
+def test_epilogue_defaults_are_the_product(oracle_mod):
+    a, b = inputs.random_operands(7, 9, 11, "bf16", seed=5)
+    ab, bb = inputs.bits(a, "bf16"), inputs.bits(b, "bf16")
+    p = oracle_mod.gemm(ab, bb, "bf16")
+    assert np.array_equal(oracle_mod.gemm_ex(ab, bb, "bf16"), p)
+    assert np.array_equal(oracle_mod.gemm_ex(ab, bb, "bf16", alpha=-4.0), -4.0 * p)
+
+
+def test_epilogue_row_bias_is_column_bias_transposed(oracle_mod):
+    rng = np.random.default_rng(3)
+    p = rng.standard_normal((5, 4))
+    bias = inputs.bits(torch.randn(5, generator=torch.Generator().manual_seed(2)).to(torch.float16), "f16")
+    r = inputs.bits(torch.randn(5, 4, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16), "bf16")
+    rows = oracle_mod.epilogue(p, alpha=0.5, beta=3.0, r_bits=r, r_dtype="bf16", bias_bits=bias,
+                               bias_dtype="f16", per_row=True, act="gelu")
+    cols = oracle_mod.epilogue(p.T, alpha=0.5, beta=3.0, r_bits=r.T, r_dtype="bf16", bias_bits=bias,
+                               bias_dtype="f16", per_row=False, act="gelu")
+    assert np.array_equal(rows, cols.T)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_epilogue_brute_force(oracle_mod, dtype):
+    """Exact rational arithmetic on tiny shapes: alpha*P + beta*R + bias (then ReLU)."""
+    rnd = random.Random(11)
+    dt = inputs.TORCH_DTYPES[dtype]
+    for trial in range(40):
+        M, N, K = rnd.randint(1, 4), rnd.randint(1, 4), rnd.randint(1, 4)
+        gen = torch.Generator().manual_seed(100 + trial)
+        a, b = torch.randn(M, K, generator=gen).to(dt), torch.randn(K, N, generator=gen).to(dt)
+        r = torch.randn(M, N, generator=gen).to(dt)
+        per_row = trial % 2 == 1
+        bias = torch.randn(M if per_row else N, generator=gen).to(dt)
+        alpha = rnd.choice([1.0, -0.5, 3.0, 0.1])
+        beta = rnd.choice([0.0, 1.0, -2.0, 0.3])
+        act = "relu" if trial % 3 == 0 else "none"
+        ab, bb, rb, biasb = (inputs.bits(t, dtype) for t in (a, b, r, bias))
+        got = oracle_mod.gemm_ex(ab, bb, dtype, alpha=alpha, beta=beta, r_bits=rb, r_dtype=dtype,
+                                 bias_bits=biasb, bias_dtype=dtype, per_row=per_row, act=act)
+        fa_ = [[brute.value(int(x), dtype) for x in row] for row in ab]
+        fb_ = [[brute.value(int(x), dtype) for x in row] for row in bb]
+        p = brute.matmul(fa_, fb_)
+        fa, fb = Fraction(float(np.float32(alpha))), Fraction(float(np.float32(beta)))
+        for i in range(M):
+            for j in range(N):
+                rv = brute.value(int(rb[i, j]), dtype)
+                v = fa * p[i][j] + fb * rv + brute.value(int(biasb[i if per_row else j]), dtype)
+                if act == "relu" and v < 0:
+                    v = Fraction(0)
+                scale = abs(fa * p[i][j]) + abs(fb * rv) + 1
+                assert abs(Fraction(float(got[i, j])) - v) <= scale * Fraction(1, 2 ** 50), (trial, i, j)
