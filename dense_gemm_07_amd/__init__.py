@@ -7,6 +7,9 @@ fallback: if the library is missing, every call raises.
     C = gemm(A, B)                      # C[M,N] = A[M,K] @ B[K,N], fp32 accumulate
     C = gemm(A, B, out_dtype=torch.float32)
     cfg, ms = autotune(A, B, out)       # benchmark candidates, cache the fastest
+    C = gemm_ex(A, B, bias=b, activation="relu")       # fused epilogue
+    C = gemm_ex(A3, B3)                 # strided batch: [batch, M, K] @ [batch, K, N]
+    Y = linear(X, W, b)                 # autograd: Y = X @ W^T + b
 """
 import ctypes
 import os
@@ -15,12 +18,14 @@ from .build import LIB
 
 __all__ = [
     "Config", "DGError", "gemm", "gemm_config", "autotune", "select_config", "candidates",
+    "Epilogue", "Batch", "gemm_ex", "autotune_ex", "workspace_size", "matmul", "linear",
     "validate", "tile_coords", "grid_shape", "cache_clear", "cache_save", "cache_load",
     "cache_size", "library", "DG_F32", "DG_F16", "DG_BF16", "VARIANT_SIMT", "VARIANT_MFMA",
 ]
 
 DG_F32, DG_F16, DG_BF16 = 0, 1, 2
 VARIANT_SIMT, VARIANT_MFMA = 0, 1
+ACTIVATIONS = {None: 0, "none": 0, "relu": 1, "gelu": 2}
 STATUS = {0: "DG_OK", 1: "DG_ERR_INVALID_VALUE", 2: "DG_ERR_UNSUPPORTED", 3: "DG_ERR_NO_CONFIG", 4: "DG_ERR_HIP"}
 
 
@@ -32,7 +37,8 @@ class DGError(RuntimeError):
 
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("block_m", "block_n", "block_k", "group_m", "waves", "stages", "variant", "xcd_remap")]
+                ("block_m", "block_n", "block_k", "group_m", "waves", "stages", "variant", "xcd_remap",
+                 "k_splits")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -42,6 +48,20 @@ class Config(ctypes.Structure):
 
     def __eq__(self, other):
         return isinstance(other, Config) and self.as_dict() == other.as_dict()
+
+
+class Epilogue(ctypes.Structure):
+    """dg_epilogue: C = act(alpha * A@B + beta * R + bias)."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("residual", ctypes.c_void_p),
+                ("residual_dtype", ctypes.c_int32), ("stride_rm", ctypes.c_int64), ("stride_rn", ctypes.c_int64),
+                ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int32), ("bias_per_row", ctypes.c_int32),
+                ("bias_stride", ctypes.c_int64), ("activation", ctypes.c_int32)]
+
+
+class Batch(ctypes.Structure):
+    """dg_batch: strided batch of products."""
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("count", "stride_a", "stride_b", "stride_c", "stride_r", "stride_bias")]
 
 
 _lib = None
@@ -61,6 +81,12 @@ def library():
         lib.dg_autotune.argtypes = _PROBLEM + [_p, _i32, ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_float)]
         lib.dg_select_config.argtypes = _PROBLEM + [ctypes.POINTER(Config), ctypes.POINTER(_i32)]
         lib.dg_validate.argtypes = _PROBLEM
+        lib.dg_gemm_ex.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch),
+                                              ctypes.POINTER(Config), _p, _i64]
+        lib.dg_autotune_ex.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch), _p, _i64,
+                                                  _i32, ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_float)]
+        lib.dg_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(Config),
+                                          ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         lib.dg_num_candidates.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.dg_num_candidates.restype = _i32
         lib.dg_get_candidate.argtypes = [_i32, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Config)]
@@ -72,6 +98,7 @@ def library():
         lib.dg_status_string.restype = ctypes.c_char_p
         lib.dg_last_error.restype = ctypes.c_char_p
         for name in ("dg_gemm", "dg_gemm_config", "dg_autotune", "dg_select_config", "dg_validate",
+                     "dg_gemm_ex", "dg_autotune_ex", "dg_workspace_size",
                      "dg_get_candidate", "dg_tile_coords", "dg_grid_shape", "dg_cache_clear",
                      "dg_cache_save", "dg_cache_load"):
             getattr(lib, name).restype = ctypes.c_int
@@ -209,3 +236,213 @@ def cache_save(path):
 
 def cache_load(path):
     _check(library().dg_cache_load(os.fsencode(path)))
+
+
+# ---- dg_gemm_ex: fused epilogue, strided batch, split-K ------------------------
+
+# Split-K workspace the binding keeps per device (zero-filled when created;
+# the library leaves its counters zero after every call). Grown on demand.
+DEFAULT_WORKSPACE_BYTES = 64 << 20
+_workspaces = {}
+
+
+def _workspace(device, nbytes):
+    import torch
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=f"cuda:{key}")
+        _workspaces[key] = ws
+    return ws
+
+
+def workspace_size(M, N, K, batch, config):
+    """(total bytes, leading counter bytes) of the split-K workspace for a config."""
+    total, counters = _i64(), _i64()
+    _check(library().dg_workspace_size(M, N, K, batch, ctypes.byref(config), ctypes.byref(total),
+                                       ctypes.byref(counters)))
+    return total.value, counters.value
+
+
+def _batched(t, name, rank):
+    """(shape, strides) of one product's view, batch stride and batch count (None if unbatched)."""
+    if t.dim() == rank:
+        return tuple(t.shape), tuple(t.stride()), 0, None
+    if t.dim() == rank + 1:
+        return tuple(t.shape[1:]), tuple(t.stride()[1:]), (t.stride(0) if t.shape[0] > 1 else 0), t.shape[0]
+    raise ValueError(f"{name} must have {rank} or {rank + 1} dimensions, got {t.dim()}")
+
+
+def _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation):
+    if a.dtype != b.dtype:
+        raise TypeError(f"A and B must share a dtype ({a.dtype} vs {b.dtype})")
+    (M, K), (sam, sak), sa, na = _batched(a, "A", 2)
+    (K2, N), (sbk, sbn), sb, nb = _batched(b, "B", 2)
+    cshape, (scm, scn), sc, nc = _batched(out, "out", 2)
+    counts = {n for n in (na, nb, nc) if n is not None}
+    if len(counts) > 1:
+        raise ValueError(f"batch sizes differ: {sorted(counts)}")
+    count = counts.pop() if counts else 1
+    if nc is None and (na is not None or nb is not None):
+        raise ValueError("a batched product needs a 3-D out")
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {tuple(a.shape)}, B is {tuple(b.shape)}")
+    if cshape != (M, N):
+        raise ValueError(f"out must be {(M, N)} per product, got {cshape}")
+    for name, t in (("A", a), ("B", b), ("out", out), ("residual", residual), ("bias", bias)):
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(k for k in ACTIVATIONS if k)}")
+    epi = Epilogue(alpha=alpha, beta=beta, activation=ACTIVATIONS[activation])
+    sr = 0
+    if residual is not None:
+        rshape, (srm, srn), sr, nr = _batched(residual, "residual", 2)
+        if nr is not None and nr != count:
+            raise ValueError("residual batch differs")
+        if rshape != (M, N):
+            raise ValueError(f"residual must be {(M, N)} per product")
+        epi.residual = residual.data_ptr()
+        epi.residual_dtype = _dtype_code(residual.dtype)
+        epi.stride_rm, epi.stride_rn = srm, srn
+    sbias = 0
+    if bias is not None:
+        (blen,), (bstride,), sbias, nbias = _batched(bias, "bias", 1)
+        if nbias is not None and nbias != count:
+            raise ValueError("bias batch differs")
+        if blen != (M if bias_per_row else N):
+            raise ValueError(f"bias must have {M if bias_per_row else N} entries")
+        epi.bias = bias.data_ptr()
+        epi.bias_dtype = _dtype_code(bias.dtype)
+        epi.bias_per_row = 1 if bias_per_row else 0
+        epi.bias_stride = bstride
+    batch = Batch(count=count, stride_a=sa, stride_b=sb, stride_c=sc, stride_r=sr, stride_bias=sbias)
+    prob = [M, N, K, a.data_ptr(), sam, sak, b.data_ptr(), sbk, sbn,
+            out.data_ptr(), scm, scn, _dtype_code(a.dtype), _dtype_code(out.dtype)]
+    return prob, epi, batch
+
+
+def _ex_out(a, b, out, out_dtype):
+    import torch
+    if out is not None:
+        return out
+    dt = out_dtype or a.dtype
+    if a.dim() == 2 and b.dim() == 2:
+        return torch.empty((a.shape[0], b.shape[1]), dtype=dt, device=a.device)
+    n = a.shape[0] if a.dim() == 3 else b.shape[0]
+    return torch.empty((n, a.shape[-2], b.shape[-1]), dtype=dt, device=a.device)
+
+
+def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=None, bias=None,
+            bias_per_row=False, activation=None, config=None, workspace=True, stream=None):
+    """C = act(alpha * A @ B + beta * R + bias), for one product or a strided batch.
+
+    a: [M, K] or [batch, M, K]; b: [K, N] or [batch, K, N] (a 2-D operand is
+    shared by the batch); out: [M, N] or [batch, M, N]. residual: None (R is
+    out's prior contents when beta != 0) or [M, N] / [batch, M, N]. bias: [N]
+    (or [M] with bias_per_row) / [batch, N]. activation: None, "relu", "gelu".
+    config: explicit Config (k_splits > 1 = split-K) or None for the library's
+    choice. workspace: True = the binding's cached split-K workspace, a uint8
+    CUDA tensor (zeroed before first use), or None/False for none.
+    """
+    out = _ex_out(a, b, out, out_dtype)
+    prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is True:
+        need = 0
+        if config is not None and config.k_splits > 1:
+            need = workspace_size(prob[0], prob[1], prob[2], batch.count, config)[0]
+        ws = _workspace(a.device, need)
+        ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    elif workspace is not None and workspace is not False:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(library().dg_gemm_ex(*prob, _stream(a, stream), ctypes.byref(epi), ctypes.byref(batch),
+                                ctypes.byref(config) if config is not None else None, ws_ptr, ws_bytes))
+    return out
+
+
+def autotune_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=None, bias=None,
+                bias_per_row=False, activation=None, workspace=True, repeats=10, stream=None):
+    """dg_autotune_ex: tune (including split-K counts with a workspace) and cache the winner."""
+    out = _ex_out(a, b, out, out_dtype)
+    prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is True:
+        ws = _workspace(a.device, 0)
+        ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    elif workspace is not None and workspace is not False:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    cfg, ms = Config(), ctypes.c_float()
+    _check(library().dg_autotune_ex(*prob, _stream(a, stream), ctypes.byref(epi), ctypes.byref(batch), ws_ptr,
+                                    ws_bytes, repeats, ctypes.byref(cfg), ctypes.byref(ms)))
+    return cfg, ms.value
+
+
+# ---- autograd --------------------------------------------------------------------
+# The backward of C = A @ B is two more products of the same kernel family,
+# taken through transposed views (strides only): dA = dC @ B^T, dB = A^T @ dC
+# ("如何用Triton手写Kernel优化矩阵乘与Flash Attention？", 性能对比与工程落地建议:
+# wrap the forward kernel in an autograd function).
+
+def _autograd_fn():
+    import torch
+
+    class _MatMul(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, a, b):
+            ctx.save_for_backward(a, b)
+            return gemm_ex(a, b)
+
+        @staticmethod
+        def backward(ctx, dc):
+            a, b = ctx.saved_tensors
+            da = db = None
+            if ctx.needs_input_grad[0]:
+                da = gemm_ex(dc, b.transpose(-1, -2))
+            if ctx.needs_input_grad[1]:
+                if a.dim() == 3 and b.dim() == 2:
+                    # shared B: dB sums over the batch, i.e. one product over the stacked rows
+                    db = gemm_ex(a.reshape(-1, a.shape[-1]).transpose(0, 1), dc.reshape(-1, dc.shape[-1]))
+                else:
+                    db = gemm_ex(a.transpose(-1, -2), dc)
+            return da, db
+
+    class _Linear(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, w, bias):
+            ctx.save_for_backward(x, w)
+            ctx.has_bias = bias is not None
+            return gemm_ex(x, w.t(), bias=bias)
+
+        @staticmethod
+        def backward(ctx, dy):
+            x, w = ctx.saved_tensors
+            dx = dw = db = None
+            if ctx.needs_input_grad[0]:
+                dx = gemm_ex(dy, w)
+            if ctx.needs_input_grad[1]:
+                dw = gemm_ex(dy.t(), x)
+            if ctx.has_bias and ctx.needs_input_grad[2]:
+                # column sums of dY as the product ones[1, rows] @ dY
+                ones = dy.new_ones((1, dy.shape[0]))
+                db = gemm_ex(ones, dy)[0]
+            return dx, dw, db
+
+    return _MatMul, _Linear
+
+
+_fns = None
+
+
+def matmul(a, b):
+    """Differentiable C = A @ B (2-D, or batched 3-D) on the HIP kernels."""
+    global _fns
+    _fns = _fns or _autograd_fn()
+    return _fns[0].apply(a, b)
+
+
+def linear(x, weight, bias=None):
+    """Differentiable Y = X @ W^T + bias (x: [rows, in], weight: [out, in], bias: [out])."""
+    global _fns
+    _fns = _fns or _autograd_fn()
+    return _fns[1].apply(x, weight, bias)

@@ -45,12 +45,29 @@ int elem_size(int dt) { return dt == DG_F32 ? 4 : 2; }
 bool dtype_ok(int dt) { return dt == DG_F32 || dt == DG_F16 || dt == DG_BF16; }
 const char *dtype_name(int dt) { return dt == DG_F32 ? "f32" : dt == DG_F16 ? "f16" : dt == DG_BF16 ? "bf16" : "?"; }
 
+// Fused epilogue of dg_gemm_ex (the defaults are a plain store).
+struct Epi {
+    float alpha = 1.0f, beta = 0.0f;
+    const void *R = nullptr;  // residual; resolved to C when beta != 0 and none is given
+    int r_dtype = DG_F32;
+    int64_t srm = 0, srn = 0;
+    const void *bias = nullptr;
+    int bias_dtype = DG_F32;
+    int per_row = 0;
+    int64_t sbias = 0;
+    int act = DG_ACT_NONE;
+    bool general() const { return alpha != 1.0f || beta != 0.0f || bias != nullptr || act != DG_ACT_NONE; }
+};
+
 struct Problem {
     int64_t M, N, K;
     const void *A, *B;
     const void *C;
     int64_t sam, sak, sbk, sbn, scm, scn;
     int in, out;
+    int64_t batch = 1;  // products of this shape
+    int64_t bsa = 0, bsb = 0, bsc = 0, bsr = 0, bsbias = 0;
+    Epi epi;
 };
 
 int64_t gcd64(int64_t a, int64_t b) {
@@ -72,6 +89,62 @@ bool injective_2d(int64_t e1, int64_t s1, int64_t e2, int64_t s2) {
     return !(s2 / g < e1 && s1 / g < e2);
 }
 
+// Spans and stride products below are formed in 128 bits: strides are
+// arbitrary int64 values.
+typedef __int128 i128;
+
+// Element span of a strided view: (e1-1)*s1 + (e2-1)*s2 + 1 (extents >= 1).
+i128 span2(int64_t e1, int64_t s1, int64_t e2, int64_t s2) {
+    return (i128)(e1 - 1) * s1 + (i128)(e2 - 1) * s2 + 1;
+}
+
+// Sufficient condition for a strided view to be injective: sorted by stride,
+// every stride is at least the span of the dimensions with smaller strides.
+bool nested(std::vector<std::pair<int64_t, int64_t>> dims) {  // (extent, stride)
+    std::sort(dims.begin(), dims.end(), [](const auto &a, const auto &b) { return a.second < b.second; });
+    i128 span = 1;
+    for (const auto &d : dims) {
+        if (d.first <= 1) continue;
+        if ((i128)d.second < span) return false;
+        span += (i128)(d.first - 1) * d.second;
+    }
+    return true;
+}
+
+// Distinct products of a batch write distinct elements of C.
+bool batch_disjoint(const Problem &p) {
+    if (p.batch <= 1) return true;
+    if ((i128)p.bsc >= span2(p.M, p.scm, p.N, p.scn)) return true;
+    return nested({{p.M, p.scm}, {p.N, p.scn}, {p.batch, p.bsc}});
+}
+
+dg_status validate_ex(const Problem &p) {
+    const bool c_used = p.M > 0 && p.N > 0 && p.batch > 0;
+    if (p.batch < 0) return fail(DG_ERR_INVALID_VALUE, "negative batch count");
+    if (p.batch > INT32_MAX) return fail(DG_ERR_UNSUPPORTED, "batch count above 2^31 - 1");
+    if (p.bsa < 0 || p.bsb < 0 || p.bsc < 0 || p.bsr < 0 || p.bsbias < 0)
+        return fail(DG_ERR_INVALID_VALUE, "negative batch stride");
+    if (c_used && !batch_disjoint(p))
+        return fail(DG_ERR_INVALID_VALUE, "batch stride %" PRId64 " makes the C matrices of the batch overlap", p.bsc);
+    const Epi &e = p.epi;
+    if (e.act != DG_ACT_NONE && e.act != DG_ACT_RELU && e.act != DG_ACT_GELU)
+        return fail(DG_ERR_INVALID_VALUE, "unknown activation %d", e.act);
+    if (e.beta != 0.0f && c_used) {
+        if (!e.R) return fail(DG_ERR_INVALID_VALUE, "residual is NULL");
+        if (!dtype_ok(e.r_dtype)) return fail(DG_ERR_INVALID_VALUE, "unknown residual dtype %d", e.r_dtype);
+        if (e.srm < 0 || e.srn < 0) return fail(DG_ERR_INVALID_VALUE, "negative residual stride");
+        if ((uintptr_t)e.R % (uintptr_t)elem_size(e.r_dtype))
+            return fail(DG_ERR_INVALID_VALUE, "residual not aligned to its element size");
+    }
+    if (e.bias && c_used) {
+        if (!dtype_ok(e.bias_dtype)) return fail(DG_ERR_INVALID_VALUE, "unknown bias dtype %d", e.bias_dtype);
+        if (e.sbias < 0) return fail(DG_ERR_INVALID_VALUE, "negative bias stride");
+        if ((uintptr_t)e.bias % (uintptr_t)elem_size(e.bias_dtype))
+            return fail(DG_ERR_INVALID_VALUE, "bias not aligned to its element size");
+    }
+    return DG_OK;
+}
+
 dg_status validate(const Problem &p) {
     if (!dtype_ok(p.in)) return fail(DG_ERR_INVALID_VALUE, "unknown input dtype %d", p.in);
     if (!dtype_ok(p.out)) return fail(DG_ERR_INVALID_VALUE, "unknown output dtype %d", p.out);
@@ -86,14 +159,15 @@ dg_status validate(const Problem &p) {
     if (c_used && (p.scm < 1 || p.scn < 1)) return fail(DG_ERR_INVALID_VALUE, "C strides must be >= 1");
     if (c_used && !injective_2d(p.M, p.scm, p.N, p.scn))
         return fail(DG_ERR_INVALID_VALUE, "C strides (%" PRId64 ", %" PRId64 ") make elements of C overlap", p.scm, p.scn);
-    if (p.M > 0 && p.K > 0 && !p.A) return fail(DG_ERR_INVALID_VALUE, "A is NULL");
-    if (p.K > 0 && p.N > 0 && !p.B) return fail(DG_ERR_INVALID_VALUE, "B is NULL");
-    if (c_used && !p.C) return fail(DG_ERR_INVALID_VALUE, "C is NULL");
+    const bool any = p.batch != 0;  // a batch of no products reads and writes nothing
+    if (any && p.M > 0 && p.K > 0 && !p.A) return fail(DG_ERR_INVALID_VALUE, "A is NULL");
+    if (any && p.K > 0 && p.N > 0 && !p.B) return fail(DG_ERR_INVALID_VALUE, "B is NULL");
+    if (any && c_used && !p.C) return fail(DG_ERR_INVALID_VALUE, "C is NULL");
     const uintptr_t ie = (uintptr_t)elem_size(p.in), oe = (uintptr_t)elem_size(p.out);
     if (((uintptr_t)p.A % ie) || ((uintptr_t)p.B % ie))
         return fail(DG_ERR_INVALID_VALUE, "A or B not aligned to its element size");
     if ((uintptr_t)p.C % oe) return fail(DG_ERR_INVALID_VALUE, "C not aligned to its element size");
-    return DG_OK;
+    return validate_ex(p);
 }
 
 // ---- layout classes --------------------------------------------------------
@@ -107,8 +181,10 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 int load_mode(const void *base, int64_t rows, int64_t K, int64_t srow, int64_t sk) {
     if (!aligned16(base)) return LD_GN;
     const int64_t lim = (int64_t)1 << 30;  // elements: 2 bytes each stays below 2^31
-    if (sk == 1 && K % 8 == 0 && (rows <= 1 || srow % 8 == 0) && 256 * srow + K < lim) return LD_KC;
-    if (srow == 1 && rows % 8 == 0 && (K <= 1 || sk % 8 == 0) && K * sk + 256 < lim) return LD_RC;
+    // The pipeline also queues up to 8 x 64 k past K (as out-of-range loads),
+    // whose offsets must not wrap either: K + 512 below.
+    if (sk == 1 && K % 8 == 0 && (rows <= 1 || srow % 8 == 0) && (i128)256 * srow + K + 512 < lim) return LD_KC;
+    if (srow == 1 && rows % 8 == 0 && (K <= 1 || sk % 8 == 0) && (i128)(K + 512) * sk + 256 < lim) return LD_RC;
     return LD_GN;
 }
 
@@ -155,8 +231,12 @@ int staged_mode(int64_t rows, int64_t K, int64_t srow, int64_t sk) {
 // register-staged kernel: contiguous operands keep 16-byte loads at any
 // alignment; an operand with no unit stride makes both use element loads.
 std::pair<int, int> mfma_modes(const Problem &p) {
-    const int la = load_mode(p.A, p.M, p.K, p.sam, p.sak);
-    const int lb = load_mode(p.B, p.N, p.K, p.sbn, p.sbk);
+    // Every product of a batch starts 16-byte aligned iff the first does and
+    // the batch stride is a multiple of 8 elements.
+    const bool a_vec = p.batch <= 1 || p.bsa % 8 == 0;
+    const bool b_vec = p.batch <= 1 || p.bsb % 8 == 0;
+    const int la = a_vec ? load_mode(p.A, p.M, p.K, p.sam, p.sak) : LD_GN;
+    const int lb = b_vec ? load_mode(p.B, p.N, p.K, p.sbn, p.sbk) : LD_GN;
     if (la != LD_GN && lb != LD_GN) return {la, lb};
     const int sa = staged_mode(p.M, p.K, p.sam, p.sak);
     const int sb = staged_mode(p.N, p.K, p.sbn, p.sbk);
@@ -245,8 +325,40 @@ DeviceInfo device_info() {
 
 // ---- heuristic ---------------------------------------------------------------
 
-dg_config heuristic(const Problem &p, int cus) {
+// ---- split-K plan ------------------------------------------------------------
+
+// K ranges of a config: ceil(K / k_splits) rounded up to whole K slices.
+struct SplitPlan {
+    int splits;
+    int k_chunk;
+};
+
+SplitPlan split_plan(int64_t K, const dg_config &cfg) {
+    const int want = cfg.k_splits < 1 ? 1 : cfg.k_splits;
+    if (want <= 1 || K <= cfg.block_k) return {1, (int)K};
+    const int64_t per = (K + want - 1) / want;
+    const int64_t chunk = (per + cfg.block_k - 1) / cfg.block_k * cfg.block_k;
+    return {(int)((K + chunk - 1) / chunk), (int)chunk};
+}
+
+// Workspace of a split launch: one arrival counter per (product, tile),
+// padded to 256 bytes, then one fp32 partial tile per (product, tile, range).
+struct WsLayout {
+    int64_t counters, total;  // bytes; total < 0: does not fit in int64
+};
+
+WsLayout ws_layout(int64_t M, int64_t N, int64_t batch, const dg_config &cfg, int splits) {
+    if (splits <= 1 || M == 0 || N == 0 || batch == 0) return {0, 0};
+    const i128 tiles = (i128)((M + cfg.block_m - 1) / cfg.block_m) * ((N + cfg.block_n - 1) / cfg.block_n) * batch;
+    const i128 cnt = (tiles * 4 + 255) / 256 * 256;
+    const i128 total = cnt + tiles * splits * cfg.block_m * cfg.block_n * 4;
+    if (total > (i128)INT64_MAX) return {-1, -1};
+    return {(int64_t)cnt, (int64_t)total};
+}
+
+dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
     const auto shapes = kernel_shapes(p.in, p.out);
+    const int64_t nb = p.batch < 1 ? 1 : p.batch;
     dg_config best{};
     bool have = false;
     if (p.in == DG_F32) {
@@ -265,7 +377,7 @@ dg_config heuristic(const Problem &p, int cus) {
         int64_t most = -1;
         for (const auto &s : shapes) {
             if (!find_kernel(s, p)) continue;
-            const int64_t tiles = ((p.M + s.block_m - 1) / s.block_m) * ((p.N + s.block_n - 1) / s.block_n);
+            const int64_t tiles = ((p.M + s.block_m - 1) / s.block_m) * ((p.N + s.block_n - 1) / s.block_n) * nb;
             if (tiles >= cus) {
                 best = s;
                 have = true;
@@ -281,16 +393,30 @@ dg_config heuristic(const Problem &p, int cus) {
     if (!have && !shapes.empty()) best = shapes.front();
     best.group_m = 8;
     best.xcd_remap = 1;
+    best.k_splits = 1;
+    // Split-K when the tiles cannot fill the GPU and each K range keeps at
+    // least four K slices.
+    if (best.variant == DG_VARIANT_MFMA && ws_bytes > 0 && p.K > 0) {
+        const int64_t tiles = ((p.M + best.block_m - 1) / best.block_m) * ((p.N + best.block_n - 1) / best.block_n) * nb;
+        int64_t s = std::min<int64_t>({(int64_t)cus / std::max<int64_t>(tiles, 1), 16, p.K / (4 * best.block_k)});
+        if (s >= 2) {
+            dg_config c = best;
+            c.k_splits = (int32_t)s;
+            const WsLayout L = ws_layout(p.M, p.N, nb, c, split_plan(p.K, c).splits);
+            if (L.total >= 0 && L.total <= ws_bytes) best = c;
+        }
+    }
     return best;
 }
 
 // ---- cache -------------------------------------------------------------------
 
 struct Key {
-    int64_t M, N, K;
+    int64_t M, N, K, batch;
     int in, out, la, lb, lc;
     bool operator<(const Key &o) const {
-        return std::tie(M, N, K, in, out, la, lb, lc) < std::tie(o.M, o.N, o.K, o.in, o.out, o.la, o.lb, o.lc);
+        return std::tie(M, N, K, batch, in, out, la, lb, lc) <
+               std::tie(o.M, o.N, o.K, o.batch, o.in, o.out, o.la, o.lb, o.lc);
     }
 };
 
@@ -298,7 +424,7 @@ std::mutex g_cache_mu;
 std::map<Key, dg_config> g_cache;
 
 Key key_of(const Problem &p) {
-    Key k{p.M, p.N, p.K, p.in, p.out, -1, -1, c_class(p)};
+    Key k{p.M, p.N, p.K, p.batch, p.in, p.out, -1, -1, c_class(p)};
     if (p.in != DG_F32) std::tie(k.la, k.lb) = mfma_modes(p);
     return k;
 }
@@ -318,11 +444,16 @@ void cache_put(const Key &k, const dg_config &c) {
 
 // ---- launch ------------------------------------------------------------------
 
-dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream) {
-    if (p.M == 0 || p.N == 0) return DG_OK;
+// Enqueues a problem (all products of its batch) with one config. A split
+// config needs `ws` (ws_bytes) laid out as ws_layout describes.
+dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream, void *ws = nullptr,
+                 int64_t ws_bytes = 0) {
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return DG_OK;
     if (cfg.block_m <= 0 || cfg.block_n <= 0 || cfg.block_k <= 0)
         return fail(DG_ERR_NO_CONFIG, "config has non-positive block sizes");
     if (cfg.group_m < 1) return fail(DG_ERR_NO_CONFIG, "config group_m must be >= 1");
+    if (cfg.k_splits > 1 && cfg.variant != DG_VARIANT_MFMA)
+        return fail(DG_ERR_NO_CONFIG, "split-K (k_splits %d) needs an MFMA config", cfg.k_splits);
     const KernelEntry *e = find_kernel(cfg, p);
     if (!e)
         return fail(DG_ERR_NO_CONFIG,
@@ -332,12 +463,20 @@ dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream) {
     const int64_t gm = (p.M + cfg.block_m - 1) / cfg.block_m;
     const int64_t gn = (p.N + cfg.block_n - 1) / cfg.block_n;
     const int64_t threads = (int64_t)cfg.waves * 64;
-    if (gm * gn * threads >= ((int64_t)1 << 32) || gm * gn >= ((int64_t)1 << 31))
-        return fail(DG_ERR_UNSUPPORTED, "too many tiles (%" PRId64 " x %" PRId64 ")", gm, gn);
+    const SplitPlan sp = split_plan(p.K, cfg);
+    const int64_t per_product = gm * gn * sp.splits;  // workgroups
+    const int64_t max_groups = std::min<int64_t>(((int64_t)1 << 31) - 1, (((int64_t)1 << 32) - 1) / threads);
+    if (gm * gn >= ((int64_t)1 << 31) || per_product > max_groups)
+        return fail(DG_ERR_UNSUPPORTED, "too many tiles (%" PRId64 " x %" PRId64 " x %d K ranges)", gm, gn, sp.splits);
+    if (sp.splits > 1) {
+        const WsLayout L = ws_layout(p.M, p.N, p.batch, cfg, sp.splits);
+        if (L.total < 0) return fail(DG_ERR_UNSUPPORTED, "split-K workspace size overflows");
+        if (!ws || ws_bytes < L.total)
+            return fail(DG_ERR_INVALID_VALUE, "split-K with %d K ranges needs a workspace of %" PRId64
+                        " bytes (given %" PRId64 ")", sp.splits, L.total, ws ? ws_bytes : (int64_t)0);
+        if ((uintptr_t)ws % 256) return fail(DG_ERR_INVALID_VALUE, "workspace not 256-byte aligned");
+    }
     GemmArgs g{};
-    g.A = p.A;
-    g.B = p.B;
-    g.C = const_cast<void *>(p.C);
     g.M = (int32_t)p.M;
     g.N = (int32_t)p.N;
     g.K = (int32_t)p.K;
@@ -353,8 +492,45 @@ dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream) {
     g.sbn = p.sbn;
     g.scm = p.scm;
     g.scn = p.scn;
-    const hipError_t err = e->launch(g, stream);
-    if (err != hipSuccess) return fail(DG_ERR_HIP, "launch of %s failed: %s", e->name, hipGetErrorString(err));
+    g.splits = sp.splits;
+    g.k_chunk = sp.k_chunk;
+    g.bsa = p.bsa;
+    g.bsb = p.bsb;
+    g.bsc = p.bsc;
+    if (sp.splits > 1) {
+        const WsLayout L = ws_layout(p.M, p.N, p.batch, cfg, sp.splits);
+        g.counters = static_cast<uint32_t *>(ws);
+        g.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + L.counters);
+    }
+    const Epi &ep = p.epi;
+    g.epi = ep.general() ? 1 : 0;
+    g.act = ep.act;
+    g.alpha = ep.alpha;
+    g.beta = ep.beta;
+    g.srm = ep.srm;
+    g.srn = ep.srn;
+    g.bsr = p.bsr;
+    g.r_dtype = ep.r_dtype;
+    g.bias_dtype = ep.bias_dtype;
+    g.sbias = ep.sbias;
+    g.bsbias = p.bsbias;
+    g.bias_per_row = ep.per_row;
+    // Products per launch: the workgroup count of one launch stays below
+    // 2^31 and its thread count below 2^32.
+    const int64_t chunk = max_groups / per_product;
+    const int ie = elem_size(p.in), oe = elem_size(p.out);
+    for (int64_t b0 = 0; b0 < p.batch; b0 += chunk) {
+        g.batch = (int32_t)std::min<int64_t>(chunk, p.batch - b0);
+        g.A = static_cast<const char *>(p.A) + (intptr_t)(b0 * p.bsa * ie);
+        g.B = static_cast<const char *>(p.B) + (intptr_t)(b0 * p.bsb * ie);
+        g.C = static_cast<char *>(const_cast<void *>(p.C)) + (intptr_t)(b0 * p.bsc * oe);
+        g.R = ep.beta != 0.0f ? static_cast<const char *>(ep.R) + (intptr_t)(b0 * p.bsr * elem_size(ep.r_dtype))
+                              : nullptr;
+        g.bias = ep.bias ? static_cast<const char *>(ep.bias) + (intptr_t)(b0 * p.bsbias * elem_size(ep.bias_dtype))
+                         : nullptr;
+        const hipError_t err = e->launch(g, stream);
+        if (err != hipSuccess) return fail(DG_ERR_HIP, "launch of %s failed: %s", e->name, hipGetErrorString(err));
+    }
     return DG_OK;
 }
 
@@ -366,12 +542,73 @@ Problem make_problem(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam
 void log_choice(const char *what, const Problem &p, const dg_config &c) {
     if (!log_enabled()) return;
     fprintf(stderr,
-            "[dg] %s M=%" PRId64 " N=%" PRId64 " K=%" PRId64 " %s->%s: block %dx%dx%d waves %d stages %d variant %d group_m %d xcd %d\n",
-            what, p.M, p.N, p.K, dtype_name(p.in), dtype_name(p.out), c.block_m, c.block_n, c.block_k, c.waves,
-            c.stages, c.variant, c.group_m, c.xcd_remap);
+            "[dg] %s M=%" PRId64 " N=%" PRId64 " K=%" PRId64 " batch=%" PRId64
+            " %s->%s: block %dx%dx%d waves %d stages %d variant %d group_m %d xcd %d k_splits %d\n",
+            what, p.M, p.N, p.K, p.batch, dtype_name(p.in), dtype_name(p.out), c.block_m, c.block_n, c.block_k,
+            c.waves, c.stages, c.variant, c.group_m, c.xcd_remap, c.k_splits);
 }
 
-dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_config *chosen, float *best_ms);
+// Fills in the epilogue and batch of dg_gemm_ex. A beta != 0 without a
+// residual reads C itself (C's dtype, strides and batch stride).
+void apply_ex(Problem &p, const dg_epilogue *ep, const dg_batch *bt) {
+    if (bt) {
+        p.batch = bt->count;
+        p.bsa = bt->stride_a;
+        p.bsb = bt->stride_b;
+        p.bsc = bt->stride_c;
+        p.bsr = bt->stride_r;
+        p.bsbias = bt->stride_bias;
+    }
+    if (ep) {
+        Epi &e = p.epi;
+        e.alpha = ep->alpha;
+        e.beta = ep->beta;
+        e.act = ep->activation;
+        e.bias = ep->bias;
+        e.bias_dtype = ep->bias_dtype;
+        e.per_row = ep->bias_per_row ? 1 : 0;
+        e.sbias = ep->bias_stride;
+        if (ep->beta != 0.0f) {
+            if (ep->residual) {
+                e.R = ep->residual;
+                e.r_dtype = ep->residual_dtype;
+                e.srm = ep->stride_rm;
+                e.srn = ep->stride_rn;
+            } else {
+                e.R = p.C;
+                e.r_dtype = p.out;
+                e.srm = p.scm;
+                e.srn = p.scn;
+                p.bsr = p.bsc;
+            }
+        }
+    }
+}
+
+// True when the epilogue reads C's own prior contents (each launch then
+// changes its own input).
+bool reads_c(const Problem &p) { return p.epi.beta != 0.0f && p.epi.R == p.C; }
+
+// The library's choice for a problem: the cached config, else the heuristic.
+// A cached split config runs unsplit when the call has no room for its
+// workspace.
+dg_config choose(const Problem &p, int64_t ws_bytes, bool *from_cache = nullptr) {
+    dg_config c;
+    const bool hit = cache_get(key_of(p), c);
+    if (hit) {
+        if (c.k_splits > 1) {
+            const WsLayout L = ws_layout(p.M, p.N, p.batch, c, split_plan(p.K, c).splits);
+            if (L.total < 0 || L.total > ws_bytes) c.k_splits = 1;
+        }
+    } else {
+        c = heuristic(p, device_info().cus, ws_bytes);
+    }
+    if (from_cache) *from_cache = hit;
+    return c;
+}
+
+dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_config *chosen, float *best_ms,
+                        void *ws = nullptr, int64_t ws_bytes = 0);
 
 }  // namespace
 }  // namespace dg
@@ -411,10 +648,8 @@ dg_status dg_select_config(int64_t M, int64_t N, int64_t K, const void *A, int64
                              C ? C : aligned_stub, scm, scn, in_dtype, out_dtype);
     dg_status s = validate(p);
     if (s != DG_OK) return s;
-    dg_config c;
-    const bool hit = cache_get(key_of(p), c);
-    if (!hit) c = heuristic(p, device_info().cus);
-    *out = c;
+    bool hit = false;
+    *out = choose(p, 0, &hit);
     if (from_cache) *from_cache = hit ? 1 : 0;
     return DG_OK;
 }
@@ -445,10 +680,58 @@ dg_status dg_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, i
             return v && strcmp(v, "1") == 0;
         }();
         if (tune_on_miss) return autotune_impl(p, (hipStream_t)stream, 0, nullptr, nullptr);
-        c = heuristic(p, device_info().cus);
     }
+    c = choose(p, 0);
     log_choice("gemm", p, c);
     return launch(p, c, (hipStream_t)stream);
+}
+
+dg_status dg_gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                     int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
+                     dg_dtype out_dtype, void *stream, const dg_epilogue *epilogue, const dg_batch *batch,
+                     const dg_config *cfg, void *workspace, int64_t workspace_bytes) {
+    g_last_error.clear();
+    if (workspace_bytes < 0) return fail(DG_ERR_INVALID_VALUE, "negative workspace size");
+    if (!workspace) workspace_bytes = 0;
+    Problem p = make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype);
+    apply_ex(p, epilogue, batch);
+    dg_status s = validate(p);
+    if (s != DG_OK) return s;
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return DG_OK;
+    const dg_config c = cfg ? *cfg : choose(p, workspace_bytes);
+    if (!cfg) log_choice("gemm_ex", p, c);
+    return launch(p, c, (hipStream_t)stream, workspace, workspace_bytes);
+}
+
+dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count, const dg_config *cfg,
+                            int64_t *bytes, int64_t *counter_bytes) {
+    g_last_error.clear();
+    if (!cfg || !bytes) return fail(DG_ERR_INVALID_VALUE, "NULL argument");
+    if (M < 0 || N < 0 || K < 0 || batch_count < 0) return fail(DG_ERR_INVALID_VALUE, "negative size");
+    if (cfg->block_m <= 0 || cfg->block_n <= 0 || cfg->block_k <= 0)
+        return fail(DG_ERR_INVALID_VALUE, "non-positive block size");
+    const WsLayout L = ws_layout(M, N, batch_count, *cfg, split_plan(K, *cfg).splits);
+    if (L.total < 0) return fail(DG_ERR_UNSUPPORTED, "workspace size overflows");
+    *bytes = L.total;
+    if (counter_bytes) *counter_bytes = L.counters;
+    return DG_OK;
+}
+
+dg_status dg_autotune_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                         int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
+                         dg_dtype out_dtype, void *stream, const dg_epilogue *epilogue, const dg_batch *batch,
+                         void *workspace, int64_t workspace_bytes, int32_t repeats, dg_config *chosen,
+                         float *best_ms) {
+    g_last_error.clear();
+    if (workspace_bytes < 0) return fail(DG_ERR_INVALID_VALUE, "negative workspace size");
+    if (!workspace) workspace_bytes = 0;
+    Problem p = make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype);
+    apply_ex(p, epilogue, batch);
+    dg_status s = validate(p);
+    if (s != DG_OK) return s;
+    if (reads_c(p) && p.M > 0 && p.N > 0 && p.batch > 0)
+        return fail(DG_ERR_INVALID_VALUE, "cannot autotune an epilogue that reads C (every trial launch changes C)");
+    return autotune_impl(p, (hipStream_t)stream, repeats, chosen, best_ms, workspace, workspace_bytes);
 }
 
 dg_status dg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
@@ -515,7 +798,7 @@ int32_t dg_cache_size(void) {
     return (int32_t)g_cache.size();
 }
 
-static const char kCacheHeader[] = "dg-config-cache 1";
+static const char kCacheHeader[] = "dg-config-cache 2";
 
 dg_status dg_cache_save(const char *path) {
     g_last_error.clear();
@@ -531,9 +814,9 @@ dg_status dg_cache_save(const char *path) {
     for (const auto &kv : snapshot) {
         const Key &k = kv.first;
         const dg_config &c = kv.second;
-        fprintf(f, "%" PRId64 " %" PRId64 " %" PRId64 " %d %d %d %d %d  %d %d %d %d %d %d %d %d\n", k.M, k.N, k.K,
-                k.in, k.out, k.la, k.lb, k.lc, c.block_m, c.block_n, c.block_k, c.group_m, c.waves, c.stages,
-                c.variant, c.xcd_remap);
+        fprintf(f, "%" PRId64 " %" PRId64 " %" PRId64 " %" PRId64 " %d %d %d %d %d  %d %d %d %d %d %d %d %d %d\n",
+                k.M, k.N, k.K, k.batch, k.in, k.out, k.la, k.lb, k.lc, c.block_m, c.block_n, c.block_k, c.group_m,
+                c.waves, c.stages, c.variant, c.xcd_remap, c.k_splits);
     }
     const bool ok = fclose(f) == 0;
     return ok ? DG_OK : fail(DG_ERR_INVALID_VALUE, "error writing %s", path);
@@ -554,11 +837,13 @@ dg_status dg_cache_load(const char *path) {
     while (fgets(line, sizeof(line), f)) {
         Key k{};
         dg_config c{};
-        const int n = sscanf(line, "%" SCNd64 " %" SCNd64 " %" SCNd64 " %d %d %d %d %d %d %d %d %d %d %d %d %d", &k.M,
-                             &k.N, &k.K, &k.in, &k.out, &k.la, &k.lb, &k.lc, &c.block_m, &c.block_n, &c.block_k,
-                             &c.group_m, &c.waves, &c.stages, &c.variant, &c.xcd_remap);
-        const bool sane = n == 16 && k.M >= 0 && k.N >= 0 && k.K >= 0 && dtype_ok(k.in) && dtype_ok(k.out) &&
-                          c.block_m > 0 && c.block_n > 0 && c.block_k > 0 && c.group_m > 0;
+        const int n = sscanf(line,
+                             "%" SCNd64 " %" SCNd64 " %" SCNd64 " %" SCNd64 " %d %d %d %d %d %d %d %d %d %d %d %d %d %d",
+                             &k.M, &k.N, &k.K, &k.batch, &k.in, &k.out, &k.la, &k.lb, &k.lc, &c.block_m, &c.block_n,
+                             &c.block_k, &c.group_m, &c.waves, &c.stages, &c.variant, &c.xcd_remap, &c.k_splits);
+        const bool sane = n == 18 && k.M >= 0 && k.N >= 0 && k.K >= 0 && k.batch >= 0 && dtype_ok(k.in) &&
+                          dtype_ok(k.out) && c.block_m > 0 && c.block_n > 0 && c.block_k > 0 && c.group_m > 0 &&
+                          c.k_splits >= 0;
         if (!sane) {
             ++bad;
             continue;
@@ -583,10 +868,15 @@ dg_status dg_cache_load(const char *path) {
 namespace dg {
 namespace {
 
-dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_config *chosen, float *best_ms) {
+// Split counts the autotuner tries when a workspace is given and the tiles
+// of a shape do not fill the GPU.
+const int kSplits[] = {2, 4, 8, 16};
+
+dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_config *chosen, float *best_ms,
+                        void *ws, int64_t ws_bytes) {
     if (repeats <= 0) repeats = 10;
-    if (p.M == 0 || p.N == 0) {
-        dg_config c = heuristic(p, device_info().cus);
+    if (p.M == 0 || p.N == 0 || p.batch == 0) {
+        dg_config c = heuristic(p, device_info().cus, ws_bytes);
         if (chosen) *chosen = c;
         if (best_ms) *best_ms = 0.0f;
         return DG_OK;
@@ -597,7 +887,23 @@ dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_co
         (void)hipEventDestroy(e0);
         return fail(DG_ERR_HIP, "hipEventCreate failed");
     }
-    const auto cands = candidates(p.in, p.out);
+    std::vector<dg_config> cands;
+    const int cus = device_info().cus;
+    for (const auto &c : candidates(p.in, p.out)) {
+        cands.push_back(c);
+        if (c.variant != DG_VARIANT_MFMA || ws_bytes <= 0) continue;
+        const int64_t tiles = ((p.M + c.block_m - 1) / c.block_m) * ((p.N + c.block_n - 1) / c.block_n) * p.batch;
+        if (tiles >= cus) continue;
+        for (int sk : kSplits) {
+            dg_config x = c;
+            x.k_splits = sk;
+            const int used = split_plan(p.K, x).splits;
+            if (used < sk && sk != kSplits[0]) continue;  // same ranges as a smaller count
+            if (used < 2) continue;
+            const WsLayout L = ws_layout(p.M, p.N, p.batch, x, used);
+            if (L.total >= 0 && L.total <= ws_bytes) cands.push_back(x);
+        }
+    }
     dg_config best{};
     float best_t = 0.0f;
     bool have = false;
@@ -606,10 +912,10 @@ dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_co
     for (const auto &c : cands) {
         if (!find_kernel(c, p)) continue;
         bool ok = true;
-        for (int w = 0; w < 2 && ok; ++w) ok = launch(p, c, stream) == DG_OK;
+        for (int w = 0; w < 2 && ok; ++w) ok = launch(p, c, stream, ws, ws_bytes) == DG_OK;
         times.clear();
         for (int r = 0; r < repeats && ok; ++r) {
-            ok = hipEventRecord(e0, stream) == hipSuccess && launch(p, c, stream) == DG_OK &&
+            ok = hipEventRecord(e0, stream) == hipSuccess && launch(p, c, stream, ws, ws_bytes) == DG_OK &&
                  hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
             float ms = 0.0f;
             ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
@@ -623,8 +929,8 @@ dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_co
         std::sort(times.begin(), times.end());
         const float med = times[times.size() / 2];
         if (log_enabled())
-            fprintf(stderr, "[dg] autotune %dx%dx%d w%d s%d g%d xcd%d: %.4f ms\n", c.block_m, c.block_n, c.block_k,
-                    c.waves, c.stages, c.group_m, c.xcd_remap, med);
+            fprintf(stderr, "[dg] autotune %dx%dx%d w%d s%d g%d xcd%d split%d: %.4f ms\n", c.block_m, c.block_n,
+                    c.block_k, c.waves, c.stages, c.group_m, c.xcd_remap, c.k_splits, med);
         if (!have || med < best_t) {
             best = c;
             best_t = med;
@@ -637,7 +943,7 @@ dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_co
     if (!have) return fail(DG_ERR_UNSUPPORTED, "no candidate kernel for %s -> %s", dtype_name(p.in), dtype_name(p.out));
     cache_put(key_of(p), best);
     log_choice("autotune winner", p, best);
-    st = launch(p, best, stream);
+    st = launch(p, best, stream, ws, ws_bytes);
     if (st != DG_OK) return st;
     if (hipStreamSynchronize(stream) != hipSuccess) return fail(DG_ERR_HIP, "hipStreamSynchronize failed");
     if (chosen) *chosen = best;

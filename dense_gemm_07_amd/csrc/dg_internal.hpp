@@ -14,6 +14,12 @@ namespace dg {
 // Runtime arguments of one launch. Sizes fit in int32 (checked on the host);
 // strides are element strides (int64: a leading dimension times a row index
 // can pass 2^31).
+//
+// One launch covers `batch` products of the same shape (product b reads
+// A + b*bsa, B + b*bsb, R + b*bsr, bias + b*bsbias and writes C + b*bsc) and
+// `splits` K ranges per output tile: range s covers k in
+// [s*k_chunk, min(K, (s+1)*k_chunk)). Workgroup ids enumerate
+// (product, range, tile) with the tile fastest.
 struct GemmArgs {
     const void *A;
     const void *B;
@@ -25,6 +31,24 @@ struct GemmArgs {
     int32_t num_xcd;
     int32_t out_dtype;  // dg_dtype of C (the MFMA kernels pick the store at run time)
     int64_t sam, sak, sbk, sbn, scm, scn;
+    // batch and split-K
+    int32_t batch;          // products in this launch, >= 1
+    int32_t splits;         // K ranges per tile, >= 1; > 1 only for the MFMA kernels
+    int32_t k_chunk;        // K elements per range (a multiple of block_k when splits > 1)
+    int64_t bsa, bsb, bsc;  // batch strides of A, B, C
+    float *ws;              // split-K partial tiles (fp32)
+    uint32_t *counters;     // split-K arrival count per (product, tile); zero between launches
+    // fused epilogue: C = act(alpha * acc + beta * R + bias)
+    int32_t epi;            // 0: C = acc (the other fields are unused); 1: the general form
+    int32_t act;            // dg_activation
+    float alpha, beta;      // beta == 0: R is not read
+    const void *R;          // residual (C itself for an in-place beta * C)
+    int64_t srm, srn, bsr;
+    int32_t r_dtype;
+    int32_t bias_dtype;
+    const void *bias;       // NULL: no bias
+    int64_t sbias, bsbias;
+    int32_t bias_per_row;   // 0: bias[j], one per column; 1: bias[i], one per row
 };
 
 // How an operand tile is fetched from global memory. The operand is viewed
@@ -78,17 +102,18 @@ DG_DECLARE_MFMA_HOOKS(f16)
 //     (the 1D decode of "Triton：04 Matmul、Autotune 与 PyTorch 集成").
 // Both steps are bijections on [0, grid_m * grid_n).
 // ---------------------------------------------------------------------------
-__host__ __device__ inline void tile_coords(int wg, int grid_m, int grid_n, int group_m,
-                                            int xcd_remap, int num_xcd, int &pid_m, int &pid_n) {
-    const int tiles = grid_m * grid_n;
-    int lid = wg;
-    if (xcd_remap && num_xcd > 1) {
-        const int x = wg % num_xcd;       // XCD this id is dispatched to
-        const int local = wg / num_xcd;   // its rank among that XCD's ids
-        const int q = tiles / num_xcd, r = tiles % num_xcd;
-        // XCDs 0..r-1 receive q+1 ids, the others q.
-        lid = x * q + (x < r ? x : r) + local;
-    }
+
+// Step 1 over `total` workgroup ids.
+__host__ __device__ inline int xcd_rank(int wg, int total, int num_xcd) {
+    const int x = wg % num_xcd;       // XCD this id is dispatched to
+    const int local = wg / num_xcd;   // its rank among that XCD's ids
+    const int q = total / num_xcd, r = total % num_xcd;
+    // XCDs 0..r-1 receive q+1 ids, the others q.
+    return x * q + (x < r ? x : r) + local;
+}
+
+// Step 2: logical tile number -> (pid_m, pid_n).
+__host__ __device__ inline void group_major(int lid, int grid_m, int grid_n, int group_m, int &pid_m, int &pid_n) {
     const int g = group_m < 1 ? 1 : group_m;
     const int per_group = g * grid_n;
     const int group_id = lid / per_group;
@@ -97,6 +122,40 @@ __host__ __device__ inline void tile_coords(int wg, int grid_m, int grid_n, int 
     const int in_group = lid - group_id * per_group;
     pid_m = first_m + in_group % rows_here;
     pid_n = in_group / rows_here;
+}
+
+__host__ __device__ inline void tile_coords(int wg, int grid_m, int grid_n, int group_m,
+                                            int xcd_remap, int num_xcd, int &pid_m, int &pid_n) {
+    const int tiles = grid_m * grid_n;
+    const int lid = (xcd_remap && num_xcd > 1) ? xcd_rank(wg, tiles, num_xcd) : wg;
+    group_major(lid, grid_m, grid_n, group_m, pid_m, pid_n);
+}
+
+// What one workgroup of a launch computes: tile (pm, pn) of product `prod`,
+// K range `split`; `slot` numbers the (product, tile) pair. The XCD
+// renumbering runs over all workgroups of the launch, so the ids one XCD
+// serves are consecutive tiles of one product and K range.
+struct WorkItem {
+    int pm, pn, split, prod, slot;
+};
+
+__host__ __device__ inline WorkItem work_item(int wg, const GemmArgs &g) {
+    const int tiles = g.grid_m * g.grid_n;
+    const int total = tiles * g.splits * g.batch;  // < 2^31, checked on the host
+    const int lid = (g.xcd_remap && g.num_xcd > 1) ? xcd_rank(wg, total, g.num_xcd) : wg;
+    WorkItem w;
+    const int t = lid % tiles;
+    const int rest = lid / tiles;
+    w.split = rest % g.splits;
+    w.prod = rest / g.splits;
+    w.slot = w.prod * tiles + t;
+    group_major(t, g.grid_m, g.grid_n, g.group_m, w.pm, w.pn);
+    return w;
+}
+
+// Workgroups of one launch.
+inline unsigned launch_groups(const GemmArgs &g) {
+    return (unsigned)g.grid_m * (unsigned)g.grid_n * (unsigned)g.splits * (unsigned)g.batch;
 }
 
 }  // namespace dg

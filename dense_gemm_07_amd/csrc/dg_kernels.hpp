@@ -11,6 +11,12 @@
 //                fp32 accumulators, a two-buffer LDS pipeline (slice s+1 is
 //                fetched while slice s is multiplied), padded LDS rows, and a
 //                masked, dtype-converting epilogue.
+//  gemm_mfma_lds -- the same tiles with operands moved global -> LDS by the
+//                buffer unit and an S-stage pipeline.
+//
+// Every kernel also serves a strided batch of products, an optional fused
+// epilogue (C = act(alpha * acc + beta * R + bias)), and -- the MFMA kernels
+// -- split-K with a deterministic reduction.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,6 +57,37 @@ template <> __device__ __forceinline__ uint16_t from_f32<BF16>(float v) {
     return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+// ---- fused epilogue ----------------------------------------------------------
+// The element-wise work after the K loop runs on the fp32 accumulator before
+// the single rounding to C's dtype, so an activation or bias costs no extra
+// pass over C ("用 Triton 写 GPU Kernel：从 Vector Add、Softmax 到 MatMul" §2.7:
+// fusion keeps intermediates on chip and saves launches).
+
+__device__ __forceinline__ float load_any(const void *p, int64_t off, int dt) {
+    if (dt == DG_BF16) return to_f32<BF16>(static_cast<const uint16_t *>(p)[off]);
+    if (dt == DG_F16) return to_f32<F16>(static_cast<const uint16_t *>(p)[off]);
+    return static_cast<const float *>(p)[off];
+}
+
+// ReLU keeps NaN and -0 (only v < 0 becomes +0). GELU is v * Phi(v) with the
+// normal CDF written through erfc, which stays accurate for large negative
+// v where 1 + erf(v / sqrt 2) would cancel.
+__device__ __forceinline__ float activate(float v, int act) {
+    if (act == DG_ACT_RELU) return v < 0.0f ? 0.0f : v;
+    if (act == DG_ACT_GELU) return 0.5f * v * erfcf(-v * 0.70710678118654752440f);
+    return v;
+}
+
+// C[gm, gn] = act(alpha * v + beta * R[gm, gn] + bias) for one element.
+// r_off / b_off are the batch offsets of R and bias.
+__device__ __forceinline__ float epilogue_value(const GemmArgs &g, float v, int gm, int gn, int64_t r_off,
+                                                int64_t b_off) {
+    float x = g.alpha * v;
+    if (g.beta != 0.0f) x = __builtin_fmaf(g.beta, load_any(g.R, r_off + (int64_t)gm * g.srm + (int64_t)gn * g.srn, g.r_dtype), x);
+    if (g.bias) x += load_any(g.bias, b_off + (int64_t)(g.bias_per_row ? gm : gn) * g.sbias, g.bias_dtype);
+    return activate(x, g.act);
+}
+
 // ============================================================================
 // gemm_simt: 256 threads, a 16 x 16 thread grid, each thread RM x RN outputs.
 // ============================================================================
@@ -62,15 +99,14 @@ __global__ __launch_bounds__(256) void gemm_simt(GemmArgs g) {
     __shared__ float As[BK][BM + 1];
     __shared__ float Bs[BK][BN + 1];
 
-    int pm, pn;
-    tile_coords(blockIdx.x, g.grid_m, g.grid_n, g.group_m, g.xcd_remap, g.num_xcd, pm, pn);
-    const int m0 = pm * BM, n0 = pn * BN;
+    const WorkItem w = work_item(blockIdx.x, g);  // the host launches this kernel with splits == 1
+    const int m0 = w.pm * BM, n0 = w.pn * BN;
     const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
     using SI = typename TI::storage;
     using SO = typename TO::storage;
-    const SI *A = static_cast<const SI *>(g.A);
-    const SI *B = static_cast<const SI *>(g.B);
-    SO *C = static_cast<SO *>(g.C);
+    const SI *A = static_cast<const SI *>(g.A) + (int64_t)w.prod * g.bsa;
+    const SI *B = static_cast<const SI *>(g.B) + (int64_t)w.prod * g.bsb;
+    SO *C = static_cast<SO *>(g.C) + (int64_t)w.prod * g.bsc;
 
     float acc[RM][RN];
 #pragma unroll
@@ -111,13 +147,17 @@ __global__ __launch_bounds__(256) void gemm_simt(GemmArgs g) {
         __syncthreads();
     }
 
+    const int64_t r_off = (int64_t)w.prod * g.bsr, b_off = (int64_t)w.prod * g.bsbias;
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
         const int gm = m0 + ty + 16 * i;
 #pragma unroll
         for (int j = 0; j < RN; ++j) {
             const int gn = n0 + tx + 16 * j;
-            if (gm < g.M && gn < g.N) C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(acc[i][j]);
+            if (gm < g.M && gn < g.N) {
+                const float v = g.epi ? epilogue_value(g, acc[i][j], gm, gn, r_off, b_off) : acc[i][j];
+                C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(v);
+            }
         }
     }
 }
@@ -297,9 +337,175 @@ struct TileLoader {
     }
 };
 
-template <typename TO>
-__device__ __forceinline__ void store_c(void *C, int64_t off, float v) {
-    static_cast<typename TO::storage *>(C)[off] = from_f32<TO>(v);
+
+// Writes the accumulator tile (lane l, register r of block (i, j) is element
+// (row_base + 32i + 8(r/4) + r%4, col_base + 32j)) to C, masked to C's view
+// unless the tile is interior. c_off is the batch offset of C.
+template <typename TO, int FM, int FN>
+__device__ __forceinline__ void store_acc(const GemmArgs &g, int64_t c_off, const f32x16 (&acc)[FM][FN],
+                                          int row_base, int col_base, bool interior) {
+    typename TO::storage *C = static_cast<typename TO::storage *>(g.C) + c_off;
+    if (interior) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int64_t cbase = (int64_t)(col_base + j * 32) * g.scn;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    C[(int64_t)gm * g.scm + cbase] = from_f32<TO>(acc[i][j][r]);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int gn = col_base + j * 32;
+                if (gn >= g.N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    if (gm < g.M) C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(acc[i][j][r]);
+                }
+            }
+    }
+}
+
+// The same tile through the fused epilogue, staged through LDS: the tile is
+// written to LDS (fp32, rows padded by 4 floats) in passes of whole 32-row
+// fragment blocks, then every thread walks the staged rows in row-major
+// order, so the residual reads and the C writes of a wave cover whole row
+// segments, and the per-element work is a compact loop instead of a fully
+// unrolled one per accumulator register. `st` is the kernel's LDS (CAP
+// bytes, free: the caller has finished the K loop).
+template <typename TO, int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
+__device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
+                                          float *st, int m0, int n0) {
+    constexpr int T = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int LDN = BN + 4;
+    constexpr int FIT = CAP / 4 / LDN;
+    constexpr int PR = FIT >= BM ? BM : (FIT / 32) * 32;  // rows per pass
+    static_assert(PR >= 32, "LDS too small to stage 32 rows of the tile");
+    constexpr int Q = BN / 4;  // 4-column groups per row
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    typename TO::storage *C = static_cast<typename TO::storage *>(g.C) + (int64_t)w.prod * g.bsc;
+    const int64_t r_off = (int64_t)w.prod * g.bsr, b_off = (int64_t)w.prod * g.bsbias;
+    for (int p0 = 0; p0 < BM; p0 += PR) {
+        __syncthreads();  // the previous pass (or the K loop) is done with the LDS
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int rb = wm * WTM + i * 32 - p0;  // block's first row within this pass
+            if (rb < 0 || rb >= PR) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    st[(rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDN + col] = acc[i][j][r];
+            }
+        }
+        __syncthreads();
+        const int rows = min(PR, g.M - m0 - p0);
+        for (int q = tid; q < rows * Q; q += T) {
+            const int row = q / Q, c4 = (q % Q) * 4;
+            const int gm = m0 + p0 + row;
+            const float4 v = *reinterpret_cast<const float4 *>(st + row * LDN + c4);
+            const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int gn = n0 + c4 + u;
+                if (gn < g.N)
+                    C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(epilogue_value(g, e[u], gm, gn, r_off, b_off));
+            }
+        }
+    }
+}
+
+// Epilogue of the MFMA kernels: plain stores straight from the accumulator
+// registers, or the fused epilogue through LDS.
+template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
+__device__ __forceinline__ void write_tile(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
+                                           float *st, int m0, int n0) {
+    if (g.epi) {
+        if (g.out_dtype == DG_BF16) store_epi<BF16, BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
+        else if (g.out_dtype == DG_F16) store_epi<F16, BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
+        else store_epi<F32, BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
+        return;
+    }
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row_base = m0 + (wave / WN) * WTM + 4 * (lane >> 5);
+    const int col_base = n0 + (wave % WN) * WTN + (lane & 31);
+    const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
+    const int64_t c_off = (int64_t)w.prod * g.bsc;
+    if (g.out_dtype == DG_BF16) store_acc<BF16, FM, FN>(g, c_off, acc, row_base, col_base, interior);
+    else if (g.out_dtype == DG_F16) store_acc<F16, FM, FN>(g, c_off, acc, row_base, col_base, interior);
+    else store_acc<F32, FM, FN>(g, c_off, acc, row_base, col_base, interior);
+}
+
+// ---- split-K reduction ---------------------------------------------------------
+// The K loop is cut into g.splits ranges, each run by its own workgroup
+// (more workgroups when a problem has few output tiles; latency is hidden
+// by having many programs in flight, "Triton：04 Matmul、Autotune 与 PyTorch
+// 集成"). Each workgroup stores its fp32 partial tile in the workspace,
+// publishes it (device-scope release), and counts its arrival on the tile's
+// counter. The workgroup that arrives last acquires, adds the partials in
+// range order 0, 1, ..., S-1 (the same order whichever arrives last, so the
+// result is deterministic), resets the counter for the next launch, and runs
+// the epilogue. No workgroup waits for another.
+//
+// Workspace layout of a partial: float4 v of thread t at [v * T + t], v over
+// (block i, block j, quarter q) = registers 4q..4q+3 of acc[i][j]; one slot of
+// S partials per (product, tile).
+template <int FM, int FN, int T>
+__device__ __forceinline__ bool split_reduce(const GemmArgs &g, const WorkItem &w, f32x16 (&acc)[FM][FN],
+                                             uint32_t *flag) {
+    constexpr int V = FM * FN * 4;
+    const int tid = threadIdx.x;
+    float4 *slot = reinterpret_cast<float4 *>(g.ws) + (int64_t)w.slot * g.splits * (V * T);
+    float4 *mine = slot + (int64_t)w.split * (V * T);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mine[((i * FN + j) * 4 + q) * T + tid] =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    __threadfence();  // this thread's partial is visible device-wide before the arrival is counted
+    __syncthreads();
+    if (tid == 0) *flag = atomicAdd(g.counters + w.slot, 1u) == (uint32_t)(g.splits - 1) ? 1u : 0u;
+    __syncthreads();
+    if (*flag == 0u) return false;
+    __threadfence();  // acquire: the other ranges' partials are visible
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int v = (i * FN + j) * 4 + q;
+                const float4 own = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                               acc[i][j][4 * q + 3]);
+                float4 sum = w.split == 0 ? own : slot[v * T + tid];
+                for (int s = 1; s < g.splits; ++s) {
+                    const float4 p = s == w.split ? own : slot[((int64_t)s * V + v) * T + tid];
+                    sum.x += p.x;
+                    sum.y += p.y;
+                    sum.z += p.z;
+                    sum.w += p.w;
+                }
+                acc[i][j][4 * q] = sum.x;
+                acc[i][j][4 * q + 1] = sum.y;
+                acc[i][j][4 * q + 2] = sum.z;
+                acc[i][j][4 * q + 3] = sum.w;
+            }
+    if (tid == 0) g.counters[w.slot] = 0u;
+    return true;
 }
 
 // WM x WN waves, each owning a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.
@@ -314,27 +520,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * LDK];
 
-    int pm, pn;
-    tile_coords(blockIdx.x, g.grid_m, g.grid_n, g.group_m, g.xcd_remap, g.num_xcd, pm, pn);
-    const int m0 = pm * BM, n0 = pn * BN;
+    const WorkItem w = work_item(blockIdx.x, g);
+    const int m0 = w.pm * BM, n0 = w.pn * BN;
+    const int k_begin = w.split * g.k_chunk;
+    const int kl = min(g.K - k_begin, g.k_chunk);  // this workgroup's K range
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
     TileLoader<BM, BK, LDK, T, LA> la;
     TileLoader<BN, BK, LDK, T, LB> lb;
-    const uint16_t *A = static_cast<const uint16_t *>(g.A);
-    const uint16_t *B = static_cast<const uint16_t *>(g.B);
-    la.base = A + (int64_t)m0 * g.sam;
+    const uint16_t *A = static_cast<const uint16_t *>(g.A) + (int64_t)w.prod * g.bsa;
+    const uint16_t *B = static_cast<const uint16_t *>(g.B) + (int64_t)w.prod * g.bsb;
+    la.base = A + (int64_t)m0 * g.sam + (int64_t)k_begin * g.sak;
     la.srow = g.sam;
     la.sk = g.sak;
     la.rows_valid = min(BM, g.M - m0);
-    la.K = g.K;
-    lb.base = B + (int64_t)n0 * g.sbn;
+    la.K = kl;
+    lb.base = B + (int64_t)n0 * g.sbn + (int64_t)k_begin * g.sbk;
     lb.srow = g.sbn;
     lb.sk = g.sbk;
     lb.rows_valid = min(BN, g.N - n0);
-    lb.K = g.K;
+    lb.K = kl;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -344,7 +551,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = (g.K + BK - 1) / BK;
+    const int nk = (kl + BK - 1) / BK;
     if (nk > 0) {
         la.load(tid, 0);
         lb.load(tid, 0);
@@ -386,28 +593,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
         __syncthreads();
     }
 
+    // the split-K arrival flag reuses the LDS (the K loop ended with a barrier)
+    if (g.splits > 1 && !split_reduce<FM, FN, T>(g, w, acc, reinterpret_cast<uint32_t *>(&lds[0][0]))) return;
+
     // Epilogue: fp32 accumulators -> C's dtype, masked to C's view.
-    const int row_base = m0 + wm * WTM + 4 * (lane >> 5);
-    const int col_base = n0 + wn * WTN + (lane & 31);
-    const int out = g.out_dtype;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int gn = col_base + j * 32;
-            if (gn >= g.N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                if (gm < g.M) {
-                    const int64_t off = (int64_t)gm * g.scm + (int64_t)gn * g.scn;
-                    const float v = acc[i][j][r];
-                    if (out == DG_BF16) store_c<BF16>(g.C, off, v);
-                    else if (out == DG_F16) store_c<F16>(g.C, off, v);
-                    else store_c<F32>(g.C, off, v);
-                }
-            }
-        }
+    write_tile<BM, BN, WM, WN, FM, FN, (int)sizeof(lds)>(g, w, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0);
 }
 
 // ============================================================================
@@ -582,38 +772,6 @@ struct DirectLoader {
     }
 };
 
-template <typename TO, int WTM, int WTN, int FM, int FN>
-__device__ __forceinline__ void store_acc(const GemmArgs &g, const f32x16 (&acc)[FM][FN], int row_base,
-                                          int col_base, bool interior) {
-    typename TO::storage *C = static_cast<typename TO::storage *>(g.C);
-    if (interior) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int64_t cbase = (int64_t)(col_base + j * 32) * g.scn;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    C[(int64_t)gm * g.scm + cbase] = from_f32<TO>(acc[i][j][r]);
-                }
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int gn = col_base + j * 32;
-                if (gn >= g.N) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (gm < g.M) C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(acc[i][j][r]);
-                }
-            }
-    }
-}
-
 // s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this
 // wave are outstanding.
 template <int N>
@@ -675,11 +833,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
     static_assert(S >= 2, "at least two stages");
 
+    // One LDS object only: the compiler proves the fragment reads independent
+    // of the in-flight LDS loads per object, and a second __shared__ variable
+    // makes it wait for every load before each read. The split-K arrival flag
+    // reuses the pipeline's LDS once the K loop is done.
     __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
-    int pm, pn;
-    tile_coords(blockIdx.x, g.grid_m, g.grid_n, g.group_m, g.xcd_remap, g.num_xcd, pm, pn);
-    const int m0 = pm * BM, n0 = pn * BN;
+    const WorkItem w = work_item(blockIdx.x, g);
+    const int m0 = w.pm * BM, n0 = w.pn * BN;
+    const int k_begin = w.split * g.k_chunk;
+    const int kl = min(g.K - k_begin, g.k_chunk);  // this workgroup's K range
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -690,8 +853,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     constexpr int LOADS_PER_SLICE = LoaderA::PER + LoaderB::PER;  // per wave
     LoaderA la;
     LoaderB lb;
-    la.init(static_cast<const uint16_t *>(g.A) + (int64_t)m0 * g.sam, g.sam, g.sak, min(BM, g.M - m0), wave, lane);
-    lb.init(static_cast<const uint16_t *>(g.B) + (int64_t)n0 * g.sbn, g.sbn, g.sbk, min(BN, g.N - n0), wave, lane);
+    la.init(static_cast<const uint16_t *>(g.A) + (int64_t)w.prod * g.bsa + (int64_t)m0 * g.sam +
+                (int64_t)k_begin * g.sak,
+            g.sam, g.sak, min(BM, g.M - m0), wave, lane);
+    lb.init(static_cast<const uint16_t *>(g.B) + (int64_t)w.prod * g.bsb + (int64_t)n0 * g.sbn +
+                (int64_t)k_begin * g.sbk,
+            g.sbn, g.sbk, min(BN, g.N - n0), wave, lane);
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -701,7 +868,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = (g.K + BK - 1) / BK;
+    const int nk = (kl + BK - 1) / BK;
     constexpr int KSUB = BK / 16;  // MFMA k-substeps per slice
     // Fragment registers, double-buffered across k-substeps: set (kk & 1)
     // holds substep kk while the other set is being filled.
@@ -717,8 +884,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     if (nk > 0) {
 #pragma unroll
         for (int s = 0; s < S - 1; ++s) {
-            la.issue(lds + s * STAGE, s * BK, g.K, wave, lane);
-            lb.issue(lds + s * STAGE + A_BYTES, s * BK, g.K, wave, lane);
+            la.issue(lds + s * STAGE, s * BK, kl, wave, lane);
+            lb.issue(lds + s * STAGE + A_BYTES, s * BK, kl, wave, lane);
         }
         wait_vmcnt<(S - 2) * LOADS_PER_SLICE>();
         stage_barrier();
@@ -745,8 +912,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
         for (int t = from; t < to; ++t) acc[t / FN][t % FN] = Mfma<TI>::run(af[set][t / FN], bf[set][t % FN], acc[t / FN][t % FN]);
     };
     auto step = [&](char *fill, const char *__restrict__ cur, const char *next, int kt) {
-        la.issue(fill, (kt + S - 1) * BK, g.K, wave, lane);
-        lb.issue(fill + A_BYTES, (kt + S - 1) * BK, g.K, wave, lane);
+        la.issue(fill, (kt + S - 1) * BK, kl, wave, lane);
+        lb.issue(fill + A_BYTES, (kt + S - 1) * BK, kl, wave, lane);
 #pragma unroll
         for (int kk = 0; kk + 1 < KSUB; ++kk) {
             fetch(cur, kk + 1, (kk & 1) ^ 1);
@@ -778,12 +945,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     }
     wait_vmcnt<0>();  // the out-of-range tail loads must land before the workgroup can exit
 
-    const int row_base = m0 + wm * WTM + 4 * (lane >> 5);
-    const int col_base = n0 + wn * WTN + (lane & 31);
-    const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
-    if (g.out_dtype == DG_BF16) store_acc<BF16, WTM, WTN, FM, FN>(g, acc, row_base, col_base, interior);
-    else if (g.out_dtype == DG_F16) store_acc<F16, WTM, WTN, FM, FN>(g, acc, row_base, col_base, interior);
-    else store_acc<F32, WTM, WTN, FM, FN>(g, acc, row_base, col_base, interior);
+    if (g.splits > 1 && !split_reduce<FM, FN, NW * 64>(g, w, acc, reinterpret_cast<uint32_t *>(lds))) return;
+
+    write_tile<BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
 }
 
 }  // namespace dg

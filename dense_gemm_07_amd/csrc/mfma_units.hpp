@@ -14,18 +14,18 @@ constexpr bool direct_to_lds() {
 
 template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
 hipError_t launch_mfma(const GemmArgs &g, hipStream_t s) {
-    const unsigned tiles = (unsigned)g.grid_m * (unsigned)g.grid_n;
+    const unsigned groups = launch_groups(g);
     if constexpr (direct_to_lds<LA, LB>())
-        hipLaunchKernelGGL((gemm_mfma_lds<TI, BM, BN, BK, WM, WN, LA, LB, S>), dim3(tiles), dim3(WM * WN * 64), 0,
+        hipLaunchKernelGGL((gemm_mfma_lds<TI, BM, BN, BK, WM, WN, LA, LB, S>), dim3(groups), dim3(WM * WN * 64), 0,
                            s, g);
     else
-        hipLaunchKernelGGL((gemm_mfma<TI, BM, BN, BK, WM, WN, LA, LB>), dim3(tiles), dim3(WM * WN * 64), 0, s, g);
+        hipLaunchKernelGGL((gemm_mfma<TI, BM, BN, BK, WM, WN, LA, LB>), dim3(groups), dim3(WM * WN * 64), 0, s, g);
     return hipGetLastError();
 }
 
 template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
 void add_mfma(std::vector<KernelEntry> &out) {
-    out.push_back(KernelEntry{dg_config{BM, BN, BK, 1, WM * WN, S, DG_VARIANT_MFMA, 0}, TI::code, -1, LA, LB,
+    out.push_back(KernelEntry{dg_config{BM, BN, BK, 1, WM * WN, S, DG_VARIANT_MFMA, 0, 1}, TI::code, -1, LA, LB,
                               &launch_mfma<TI, BM, BN, BK, WM, WN, LA, LB, S>,
                               direct_to_lds<LA, LB>() ? "gemm_mfma_lds" : "gemm_mfma"});
 }

@@ -5,13 +5,12 @@ namespace dg {
 
 template <typename TI, typename TO, int BM, int BN, int BK>
 static hipError_t launch_simt(const GemmArgs &g, hipStream_t s) {
-    const unsigned tiles = (unsigned)g.grid_m * (unsigned)g.grid_n;
-    hipLaunchKernelGGL((gemm_simt<TI, TO, BM, BN, BK>), dim3(tiles), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemm_simt<TI, TO, BM, BN, BK>), dim3(launch_groups(g)), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 #define DG_SIMT(TI, TO, BM, BN, BK)                                                          \
-    out.push_back(KernelEntry{dg_config{BM, BN, BK, 1, 4, 1, DG_VARIANT_SIMT, 0}, TI::code,  \
+    out.push_back(KernelEntry{dg_config{BM, BN, BK, 1, 4, 1, DG_VARIANT_SIMT, 0, 1}, TI::code,  \
                               TO::code, -1, -1, &launch_simt<TI, TO, BM, BN, BK>,            \
                               "simt_" #TI "_" #TO "_" #BM "x" #BN "x" #BK})
 #define DG_SIMT_TILES(TI, TO) \

@@ -29,8 +29,9 @@
  *  - A and B are read only inside their M x K / K x N views; elements past a
  *    ragged edge count as zero (the masked load with other = 0 of the
  *    pages' kernels). Every element of C's M x N view is written exactly
- *    once; nothing else in C's allocation is written. C is overwritten
- *    (there is no alpha/beta).
+ *    once; nothing else in C's allocation is written. dg_gemm and
+ *    dg_gemm_config overwrite C; dg_gemm_ex adds alpha, beta, a residual, a
+ *    bias and an activation.
  *  - M == 0 or N == 0: returns DG_OK and launches nothing. K == 0: C is
  *    filled with +0 (the empty sum).
  *  - stream is a hipStream_t (NULL = the legacy default stream). Work is
@@ -86,6 +87,11 @@ enum {
  *  variant:   DG_VARIANT_*.
  *  xcd_remap: 1 = reorder workgroup ids so the tiles dispatched to one XCD
  *             (one L2) are consecutive in the group-major order.
+ *  k_splits:  1 (or 0) = one workgroup walks all of K for its tile; S > 1 =
+ *             split-K: S workgroups per tile each walk one K range of
+ *             block_k-multiple length and the last to finish sums the S fp32
+ *             partials in split order (deterministic) before the epilogue.
+ *             Needs a workspace (dg_gemm_ex); MFMA kernels only.
  */
 typedef struct dg_config {
     int32_t block_m, block_n, block_k;
@@ -94,6 +100,7 @@ typedef struct dg_config {
     int32_t stages;
     int32_t variant;
     int32_t xcd_remap;
+    int32_t k_splits;
 } dg_config;
 
 /*
@@ -139,6 +146,121 @@ dg_status dg_autotune(int64_t M, int64_t N, int64_t K,
                       void *C, int64_t stride_cm, int64_t stride_cn,
                       dg_dtype in_dtype, dg_dtype out_dtype, void *stream,
                       int32_t repeats, dg_config *chosen, float *best_ms);
+
+/* Activation applied last by a fused epilogue. */
+typedef enum dg_activation {
+    DG_ACT_NONE = 0,
+    DG_ACT_RELU = 1,  /* v < 0 ? +0 : v (NaN and -0 pass through) */
+    DG_ACT_GELU = 2   /* v * Phi(v), Phi the standard normal CDF (the erf form) */
+} dg_activation;
+
+/*
+ * Fused epilogue:
+ *
+ *   C[i][j] = act(alpha * (A @ B)[i][j] + beta * R[i][j] + bias)
+ *
+ * evaluated in fp32 on the fp32 accumulator, then rounded once to C's dtype
+ * (RNE). This is the element-wise work that follows the product when it
+ * stands in for a linear layer ("如何用Triton手写Kernel优化矩阵乘与Flash
+ * Attention？", 性能对比与工程落地建议), fused into the kernel that produces it
+ * so the intermediate never goes to memory ("用 Triton 写 GPU Kernel：从 Vector
+ * Add、Softmax 到 MatMul", §2.7).
+ *  alpha:          scales the product.
+ *  beta:           scales the residual R. beta == 0: R is not read at all
+ *                  (so C's prior contents may be uninitialised, even NaN).
+ *  residual:       NULL: R is C's prior contents (C's dtype and strides,
+ *                  an in-place C = alpha*AB + beta*C). Else a DEVICE matrix
+ *                  of residual_dtype with element strides (stride_rm,
+ *                  stride_rn) >= 0 that must not overlap C's view.
+ *  bias:           NULL, or a DEVICE vector of bias_dtype with element
+ *                  stride bias_stride (>= 0): bias[j] for column j (length N)
+ *                  if bias_per_row == 0, else bias[i] for row i (length M).
+ *  activation:     dg_activation.
+ * A NULL dg_epilogue means alpha = 1, beta = 0, no bias, no activation.
+ */
+typedef struct dg_epilogue {
+    float alpha;
+    float beta;
+    const void *residual;
+    int32_t residual_dtype;
+    int64_t stride_rm, stride_rn;
+    const void *bias;
+    int32_t bias_dtype;
+    int32_t bias_per_row;
+    int64_t bias_stride;
+    int32_t activation;
+} dg_epilogue;
+
+/*
+ * Strided batch of `count` independent products of the same shape:
+ * product b reads A + b*stride_a, B + b*stride_b, residual + b*stride_r,
+ * bias + b*stride_bias and writes C + b*stride_c (element strides, >= 0; 0
+ * shares an operand across the batch). The C matrices of different products
+ * must not overlap: with count > 1, C's (batch, row, column) strides sorted
+ * by size must nest (each at least the span of the smaller ones), or
+ * stride_c must be at least the span of one C view. count == 0 is a no-op.
+ * A NULL dg_batch means count = 1. The transposed products of a backward
+ * pass (dA = dC B^T, dB = A^T dC) are plain calls with swapped strides.
+ */
+typedef struct dg_batch {
+    int64_t count;
+    int64_t stride_a, stride_b, stride_c;
+    int64_t stride_r, stride_bias;
+} dg_batch;
+
+/*
+ * The general entry point: dg_gemm / dg_gemm_config plus an optional fused
+ * epilogue, an optional strided batch, an optional explicit config (NULL:
+ * the library's choice, as dg_gemm) and an optional workspace.
+ *
+ * workspace / workspace_bytes: DEVICE memory, 256-byte aligned, that the
+ * kernels use for split-K (config k_splits > 1, see dg_workspace_size).
+ * NULL / 0 if none. With cfg == NULL and a workspace, the library may choose
+ * split-K for problems with few output tiles when the workspace is large
+ * enough; without one it never splits. The leading counter bytes of the
+ * workspace (dg_workspace_size) must be zero before the first call that
+ * uses it (a zero-filled allocation); each call leaves them zero again when
+ * it completes. Calls that share a workspace must not run concurrently
+ * (issue them on one stream, or synchronise). The library never allocates.
+ * An explicit config with k_splits > 1 and no (or too small a) workspace is
+ * DG_ERR_INVALID_VALUE; with a SIMT config it is DG_ERR_NO_CONFIG.
+ */
+dg_status dg_gemm_ex(int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t stride_am, int64_t stride_ak,
+                     const void *B, int64_t stride_bk, int64_t stride_bn,
+                     void *C, int64_t stride_cm, int64_t stride_cn,
+                     dg_dtype in_dtype, dg_dtype out_dtype, void *stream,
+                     const dg_epilogue *epilogue, const dg_batch *batch,
+                     const dg_config *cfg, void *workspace, int64_t workspace_bytes);
+
+/*
+ * dg_autotune for a dg_gemm_ex problem (epilogue and batch included in every
+ * timed launch). With a workspace, the candidates also include split-K
+ * counts (2, 4, 8, 16) for tile shapes that do not fill the GPU. The winner
+ * is cached under (M, N, K, batch count, dtypes, layouts); a later dg_gemm_ex
+ * with cfg == NULL uses it (unsplit if that call's workspace is too small).
+ * An epilogue that reads C (beta != 0 and no separate residual) is
+ * rejected with DG_ERR_INVALID_VALUE: every trial launch would change C.
+ */
+dg_status dg_autotune_ex(int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t stride_am, int64_t stride_ak,
+                         const void *B, int64_t stride_bk, int64_t stride_bn,
+                         void *C, int64_t stride_cm, int64_t stride_cn,
+                         dg_dtype in_dtype, dg_dtype out_dtype, void *stream,
+                         const dg_epilogue *epilogue, const dg_batch *batch,
+                         void *workspace, int64_t workspace_bytes,
+                         int32_t repeats, dg_config *chosen, float *best_ms);
+
+/*
+ * Workspace bytes config `cfg` needs for an M x N x K problem with
+ * `batch_count` products: 0 when it does not split K. *counter_bytes (may be
+ * NULL) receives the size of the leading counter region that must start
+ * zeroed. K is cut into ranges of k_chunk = block_k * ceil(ceil(K /
+ * k_splits) / block_k) elements; the ranges actually used number
+ * ceil(K / k_chunk) (at most k_splits; 1 when K <= block_k).
+ */
+dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count, const dg_config *cfg,
+                            int64_t *bytes, int64_t *counter_bytes);
 
 /*
  * The config dg_gemm would use, without any GPU work. The pointers are only

@@ -87,3 +87,37 @@ def sample_indices(M, N, n_random=2048, seed=0):
     rows = np.concatenate([rr.ravel(), rng.integers(0, M, n_random)])
     cols = np.concatenate([cc.ravel(), rng.integers(0, N, n_random)])
     return rows, cols
+
+
+def epilogue_tolerance(K, in_dtype, out_dtype, got, ref, alpha, terms, act):
+    """Allowed |C_gpu - C_ref| for act(alpha * P + beta * R + bias).
+
+    The product's own error (tolerance above, before rounding) scaled by
+    |alpha|; the fp32 multiply, fused multiply-add and add of the epilogue
+    each round once, bounded by 2^-22 * terms, where terms = |alpha*P| +
+    |beta*R| + |bias| (fp64); ReLU is 1-Lipschitz; GELU's slope is below
+    1.13 and its fp32 evaluation adds a few ulp of the result (2^-19 relative
+    plus 2^-40 absolute); then half an ulp of the output dtype.
+    """
+    base = (1e-5 if in_dtype == "f32" else 1e-3) * math.sqrt(max(K, 1))
+    pre = abs(float(alpha)) * base + 2.0 ** -22 * np.asarray(terms, dtype=np.float64)
+    mag = np.maximum(np.abs(got), np.abs(ref))
+    if act == "gelu":
+        pre = 1.13 * pre + 2.0 ** -19 * mag + 2.0 ** -40
+    return pre + 0.5 * ulp(out_dtype, mag)
+
+
+def assert_within_tol(got, ref, tol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    same_nan = np.isnan(got) & np.isnan(ref)
+    assert np.all(np.isfinite(got) | same_nan), f"{what}: non-finite output"
+    err = np.where(same_nan, 0.0, np.abs(got - ref))
+    bad = err > tol
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
+                             f"max err {err.max():.3e}; first bad {idx.tolist()} "
+                             f"got {got[tuple(idx[0])]} ref {ref[tuple(idx[0])]}")
+    return float(err.max()) if err.size else 0.0

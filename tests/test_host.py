@@ -174,28 +174,40 @@ def test_candidate_index_out_of_range():
 
 def test_cache_load_select_save_roundtrip(tmp_path):
     dg.cache_clear()
-    # key: M N K in out la lb lc | block_m block_n block_k group_m waves stages variant xcd
+    # key: M N K batch in out la lb lc | block_m block_n block_k group_m waves stages variant xcd k_splits
     f = tmp_path / "cache.txt"
-    f.write_text("dg-config-cache 1\n"
-                 "4096 4096 4096 2 2 0 1 0  128 128 64 4 4 2 1 0\n"
+    f.write_text("dg-config-cache 2\n"
+                 "4096 4096 4096 1 2 2 0 1 0  128 128 64 4 4 2 1 0 1\n"
+                 "1024 1024 1024 1 2 2 0 1 0  128 128 64 8 4 2 1 1 4\n"
                  "this line is garbage\n")
     dg.cache_load(str(f))
-    assert dg.cache_size() == 1
+    assert dg.cache_size() == 2
     assert b"malformed" in dg.library().dg_last_error()
     c, hit = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (4096, 1), (4096, 1), BF16, BF16)
     assert hit and (c.block_m, c.block_n, c.group_m, c.xcd_remap) == (128, 128, 4, 0)
     # a different layout class of B is a different key
     _, hit2 = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (1, 4096), (4096, 1), BF16, BF16)
     assert not hit2
+    # a cached split-K config runs unsplit where the call has no workspace
+    c3, hit3 = dg.select_config_raw(1024, 1024, 1024, (1024, 1), (1024, 1), (1024, 1), BF16, BF16)
+    assert hit3 and (c3.block_m, c3.k_splits) == (128, 1)
     out = tmp_path / "saved.txt"
     dg.cache_save(str(out))
     lines = out.read_text().splitlines()
-    assert lines[0] == "dg-config-cache 1" and len(lines) == 2
+    assert lines[0] == "dg-config-cache 2" and len(lines) == 3
+    assert any(ln.split()[-1] == "4" for ln in lines[1:])  # k_splits survives the round trip
     dg.cache_clear()
     assert dg.cache_size() == 0
     dg.cache_load(str(out))
-    assert dg.cache_size() == 1
+    assert dg.cache_size() == 2
     dg.cache_clear()
+
+
+def test_cache_load_rejects_older_format(tmp_path):
+    f = tmp_path / "v1.txt"
+    f.write_text("dg-config-cache 1\n4096 4096 4096 2 2 0 1 0  128 128 64 4 4 2 1 0\n")
+    with pytest.raises(dg.DGError):
+        dg.cache_load(str(f))
 
 
 def test_cache_load_rejects_foreign_file(tmp_path):
@@ -205,3 +217,93 @@ def test_cache_load_rejects_foreign_file(tmp_path):
         dg.cache_load(str(f))
     with pytest.raises(dg.DGError):
         dg.cache_load(str(tmp_path / "missing.txt"))
+
+
+# ---- dg_gemm_ex: argument checks that fail before any GPU work ------------------
+
+FAKE = 1 << 20  # a 256-byte aligned stand-in address; never dereferenced on these paths
+
+
+def gemm_ex_status(M=64, N=64, K=64, a=(64, 1), b=(64, 1), c=(64, 1), epi=None, batch=None, cfg=None,
+                   ws=None, ws_bytes=0, dt=BF16, out=BF16):
+    lib = dg.library()
+    return lib.dg_gemm_ex(M, N, K, FAKE, *a, FAKE, *b, FAKE, *c, dt, out, None,
+                          ctypes.byref(epi) if epi else None, ctypes.byref(batch) if batch else None,
+                          ctypes.byref(cfg) if cfg else None, ws, ws_bytes)
+
+
+def mfma_cfg(bm=128, bn=128, bk=64, splits=1):
+    for c in dg.candidates(BF16, BF16):
+        if (c.block_m, c.block_n, c.block_k, c.stages) == (bm, bn, bk, 2):
+            c.k_splits = splits
+            return c
+    raise LookupError
+
+
+def test_gemm_ex_rejects_bad_epilogue():
+    assert gemm_ex_status(epi=dg.Epilogue(alpha=1.0, activation=7)) == INVALID
+    assert gemm_ex_status(epi=dg.Epilogue(alpha=1.0, bias=FAKE, bias_dtype=9)) == INVALID
+    assert gemm_ex_status(epi=dg.Epilogue(alpha=1.0, bias=FAKE + 1, bias_dtype=F32)) == INVALID  # misaligned
+    assert gemm_ex_status(epi=dg.Epilogue(alpha=1.0, bias=FAKE, bias_dtype=F32, bias_stride=-1)) == INVALID
+    assert gemm_ex_status(epi=dg.Epilogue(alpha=1.0, beta=1.0, residual=FAKE, residual_dtype=F32,
+                                          stride_rm=-1, stride_rn=1)) == INVALID
+    assert gemm_ex_status(epi=dg.Epilogue(alpha=1.0, beta=1.0, residual=FAKE, residual_dtype=5)) == INVALID
+    assert gemm_ex_status(epi=dg.Epilogue(alpha=1.0, beta=1.0, residual=FAKE + 2, residual_dtype=F32,
+                                          stride_rm=64, stride_rn=1)) == INVALID
+    assert b"residual" in dg.library().dg_last_error()
+
+
+def test_gemm_ex_rejects_bad_batch():
+    assert gemm_ex_status(batch=dg.Batch(count=-1)) == INVALID
+    assert gemm_ex_status(batch=dg.Batch(count=2, stride_a=-8)) == INVALID
+    # C views of the two products overlap (stride_c smaller than one 64x64 view, not nested)
+    assert gemm_ex_status(batch=dg.Batch(count=2, stride_c=32)) == INVALID
+    assert b"overlap" in dg.library().dg_last_error()
+    # an empty batch is a no-op, even with NULL pointers
+    lib = dg.library()
+    assert lib.dg_gemm_ex(64, 64, 64, None, 64, 1, None, 64, 1, None, 64, 1, BF16, BF16, None, None,
+                          ctypes.byref(dg.Batch(count=0)), None, None, 0) == OK
+
+
+def test_gemm_ex_split_k_argument_errors():
+    cfg = mfma_cfg(splits=4)
+    # no workspace / too small / misaligned
+    assert gemm_ex_status(K=4096, cfg=cfg) == INVALID
+    assert b"workspace" in dg.library().dg_last_error()
+    assert gemm_ex_status(K=4096, cfg=cfg, ws=FAKE, ws_bytes=1024) == INVALID
+    need = dg.workspace_size(64, 64, 4096, 1, cfg)[0]
+    assert gemm_ex_status(K=4096, cfg=cfg, ws=FAKE + 16, ws_bytes=need) == INVALID
+    assert gemm_ex_status(K=4096, cfg=cfg, ws=FAKE, ws_bytes=-5) == INVALID
+    # split-K is an MFMA feature
+    simt = [c for c in dg.candidates(F32, F32) if c.variant == dg.VARIANT_SIMT][0]
+    simt.k_splits = 2
+    assert gemm_ex_status(K=4096, cfg=simt, dt=F32, out=F32, a=(4096, 1), b=(64, 1)) == NO_CONFIG
+
+
+def test_workspace_size_arithmetic():
+    cfg = mfma_cfg(128, 128, 64, splits=4)
+    # 8 x 8 tiles, K ranges of 256: 4 ranges; counters 64*4 B padded to 256
+    assert dg.workspace_size(1024, 1024, 1024, 1, cfg) == (256 + 64 * 4 * 128 * 128 * 4, 256)
+    # batch multiplies tiles; counters 3*64*4 = 768 B
+    assert dg.workspace_size(1024, 1024, 1024, 3, cfg) == (768 + 3 * 64 * 4 * 128 * 128 * 4, 768)
+    # K = 200, 3 requested: chunks of ceil(67/64)*64 = 128 -> 2 ranges
+    cfg3 = mfma_cfg(128, 128, 64, splits=3)
+    assert dg.workspace_size(128, 128, 200, 1, cfg3) == (256 + 2 * 128 * 128 * 4, 256)
+    # one K slice or no split: nothing
+    assert dg.workspace_size(1024, 1024, 64, 1, cfg) == (0, 0)
+    assert dg.workspace_size(1024, 1024, 4096, 1, mfma_cfg(splits=1)) == (0, 0)
+    assert dg.workspace_size(0, 1024, 4096, 1, cfg) == (0, 0)
+
+
+def test_select_config_never_splits_without_workspace():
+    for M, N, K in [(16, 4096, 8192), (128, 128, 65536), (1, 1, 1 << 20)]:
+        c, _ = dg.select_config_raw(M, N, K, (K, 1), (N, 1), (N, 1), BF16, BF16)
+        assert c.k_splits == 1
+
+
+def test_autotune_ex_rejects_epilogue_reading_c():
+    lib = dg.library()
+    epi = dg.Epilogue(alpha=1.0, beta=0.5)
+    st = lib.dg_autotune_ex(64, 64, 64, FAKE, 64, 1, FAKE, 64, 1, FAKE, 64, 1, BF16, BF16, None,
+                            ctypes.byref(epi), None, None, 0, 1, None, None)
+    assert st == INVALID and b"reads C" in lib.dg_last_error()
