@@ -18,7 +18,7 @@ from .build import LIB
 
 __all__ = [
     "Config", "DGError", "gemm", "gemm_config", "autotune", "select_config", "candidates",
-    "Epilogue", "Batch", "gemm_ex", "autotune_ex", "workspace_size", "matmul", "linear",
+    "Epilogue", "Batch", "gemm_ex", "autotune_ex", "workspace_size", "select_config_ex", "matmul", "linear",
     "validate", "tile_coords", "grid_shape", "cache_clear", "cache_save", "cache_load",
     "cache_size", "library", "DG_F32", "DG_F16", "DG_BF16", "VARIANT_SIMT", "VARIANT_MFMA",
 ]
@@ -80,13 +80,14 @@ def library():
         lib.dg_gemm_config.argtypes = _PROBLEM + [_p, ctypes.POINTER(Config)]
         lib.dg_autotune.argtypes = _PROBLEM + [_p, _i32, ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_float)]
         lib.dg_select_config.argtypes = _PROBLEM + [ctypes.POINTER(Config), ctypes.POINTER(_i32)]
+        lib.dg_select_config_ex.argtypes = _PROBLEM + [ctypes.POINTER(Batch), _i64, ctypes.POINTER(Config),
+                                                       ctypes.POINTER(_i32)]
         lib.dg_validate.argtypes = _PROBLEM
         lib.dg_gemm_ex.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch),
                                               ctypes.POINTER(Config), _p, _i64]
         lib.dg_autotune_ex.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch), _p, _i64,
                                                   _i32, ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_float)]
-        lib.dg_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(Config),
-                                          ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+        lib.dg_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(Config), ctypes.POINTER(_i64)]
         lib.dg_num_candidates.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.dg_num_candidates.restype = _i32
         lib.dg_get_candidate.argtypes = [_i32, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Config)]
@@ -97,7 +98,8 @@ def library():
         lib.dg_cache_size.restype = _i32
         lib.dg_status_string.restype = ctypes.c_char_p
         lib.dg_last_error.restype = ctypes.c_char_p
-        for name in ("dg_gemm", "dg_gemm_config", "dg_autotune", "dg_select_config", "dg_validate",
+        for name in ("dg_gemm", "dg_gemm_config", "dg_autotune", "dg_select_config", "dg_select_config_ex",
+                     "dg_validate",
                      "dg_gemm_ex", "dg_autotune_ex", "dg_workspace_size",
                      "dg_get_candidate", "dg_tile_coords", "dg_grid_shape", "dg_cache_clear",
                      "dg_cache_save", "dg_cache_load"):
@@ -191,6 +193,19 @@ def select_config_raw(M, N, K, strides_a, strides_b, strides_c, in_dtype, out_dt
     return cfg, bool(hit.value)
 
 
+def select_config_ex(M, N, K, strides_a, strides_b, strides_c, in_dtype, out_dtype, batch=1,
+                     workspace_bytes=0, batch_strides=(0, 0, 0), ptr_a=0, ptr_b=0, ptr_c=0):
+    """The config gemm_ex would choose (no GPU work) for `batch` products and a workspace size."""
+    cfg, hit = Config(), _i32()
+    bt = Batch(count=batch, stride_a=batch_strides[0], stride_b=batch_strides[1], stride_c=batch_strides[2])
+    if batch > 1 and batch_strides == (0, 0, 0):
+        bt.stride_c = M * N  # a dense stack of C matrices
+    _check(library().dg_select_config_ex(M, N, K, ptr_a or None, *strides_a, ptr_b or None, *strides_b,
+                                         ptr_c or None, *strides_c, in_dtype, out_dtype, ctypes.byref(bt),
+                                         workspace_bytes, ctypes.byref(cfg), ctypes.byref(hit)))
+    return cfg, bool(hit.value)
+
+
 def validate(M, N, K, ptr_a, strides_a, ptr_b, strides_b, ptr_c, strides_c, in_dtype, out_dtype):
     """Status code of the argument check dg_gemm performs (0 = DG_OK); no GPU work."""
     lib = library()
@@ -240,8 +255,7 @@ def cache_load(path):
 
 # ---- dg_gemm_ex: fused epilogue, strided batch, split-K ------------------------
 
-# Split-K workspace the binding keeps per device (zero-filled when created;
-# the library leaves its counters zero after every call). Grown on demand.
+# Split-K workspace the binding keeps per device, grown on demand.
 DEFAULT_WORKSPACE_BYTES = 64 << 20
 _workspaces = {}
 
@@ -251,17 +265,16 @@ def _workspace(device, nbytes):
     key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=f"cuda:{key}")
+        ws = torch.empty(max(nbytes, DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=f"cuda:{key}")
         _workspaces[key] = ws
     return ws
 
 
 def workspace_size(M, N, K, batch, config):
-    """(total bytes, leading counter bytes) of the split-K workspace for a config."""
-    total, counters = _i64(), _i64()
-    _check(library().dg_workspace_size(M, N, K, batch, ctypes.byref(config), ctypes.byref(total),
-                                       ctypes.byref(counters)))
-    return total.value, counters.value
+    """Bytes of split-K workspace a config needs (0 if it does not split K)."""
+    total = _i64()
+    _check(library().dg_workspace_size(M, N, K, batch, ctypes.byref(config), ctypes.byref(total)))
+    return total.value
 
 
 def _batched(t, name, rank):
@@ -342,8 +355,8 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
     out's prior contents when beta != 0) or [M, N] / [batch, M, N]. bias: [N]
     (or [M] with bias_per_row) / [batch, N]. activation: None, "relu", "gelu".
     config: explicit Config (k_splits > 1 = split-K) or None for the library's
-    choice. workspace: True = the binding's cached split-K workspace, a uint8
-    CUDA tensor (zeroed before first use), or None/False for none.
+    choice. workspace: True = the binding's cached split-K workspace, a CUDA
+    tensor of any dtype, or None/False for none.
     """
     out = _ex_out(a, b, out, out_dtype)
     prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
@@ -351,7 +364,7 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
     if workspace is True:
         need = 0
         if config is not None and config.k_splits > 1:
-            need = workspace_size(prob[0], prob[1], prob[2], batch.count, config)[0]
+            need = workspace_size(prob[0], prob[1], prob[2], batch.count, config)
         ws = _workspace(a.device, need)
         ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     elif workspace is not None and workspace is not False:

@@ -341,19 +341,19 @@ SplitPlan split_plan(int64_t K, const dg_config &cfg) {
     return {(int)((K + chunk - 1) / chunk), (int)chunk};
 }
 
-// Workspace of a split launch: one arrival counter per (product, tile),
-// padded to 256 bytes, then one fp32 partial tile per (product, tile, range).
+// Workspace of a split launch: one fp32 partial tile per (product, tile,
+// range). Nothing in it needs initialising (every partial is written before
+// it is read, by an earlier kernel on the same stream).
 struct WsLayout {
-    int64_t counters, total;  // bytes; total < 0: does not fit in int64
+    int64_t total;  // bytes; < 0: does not fit in int64
 };
 
 WsLayout ws_layout(int64_t M, int64_t N, int64_t batch, const dg_config &cfg, int splits) {
-    if (splits <= 1 || M == 0 || N == 0 || batch == 0) return {0, 0};
+    if (splits <= 1 || M == 0 || N == 0 || batch == 0) return {0};
     const i128 tiles = (i128)((M + cfg.block_m - 1) / cfg.block_m) * ((N + cfg.block_n - 1) / cfg.block_n) * batch;
-    const i128 cnt = (tiles * 4 + 255) / 256 * 256;
-    const i128 total = cnt + tiles * splits * cfg.block_m * cfg.block_n * 4;
-    if (total > (i128)INT64_MAX) return {-1, -1};
-    return {(int64_t)cnt, (int64_t)total};
+    const i128 total = tiles * splits * cfg.block_m * cfg.block_n * 4;
+    if (total > (i128)INT64_MAX) return {-1};
+    return {(int64_t)total};
 }
 
 dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
@@ -373,8 +373,9 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
     } else {
         // The first registered shape (best first) that has a kernel for this
         // problem's layouts and gives at least one tile per CU; else the
-        // first usable shape with the most tiles.
-        int64_t most = -1;
+        // usable shape with the most tiles, and among those the least padded
+        // area (the first such in registry order).
+        int64_t most = -1, area = 0;
         for (const auto &s : shapes) {
             if (!find_kernel(s, p)) continue;
             const int64_t tiles = ((p.M + s.block_m - 1) / s.block_m) * ((p.N + s.block_n - 1) / s.block_n) * nb;
@@ -383,8 +384,10 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
                 have = true;
                 break;
             }
-            if (tiles > most) {
+            const int64_t padded = tiles * s.block_m * s.block_n;
+            if (tiles > most || (tiles == most && padded < area)) {
                 most = tiles;
+                area = padded;
                 best = s;
                 have = true;
             }
@@ -394,11 +397,18 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
     best.group_m = 8;
     best.xcd_remap = 1;
     best.k_splits = 1;
-    // Split-K when the tiles cannot fill the GPU and each K range keeps at
-    // least four K slices.
+    // Split-K (measured on MI355X, 64x64 tiles): S ranges pay when the tiles
+    // leave CUs idle and each range keeps >= 1024 of K, so S = CUs / tiles,
+    // capped by K / 1024 and 16; with K >= 8192 two ranges pay even when the
+    // tiles just fill the CUs, if two workgroups fit per CU (LDS of 160 KiB
+    // per CU). Below that the second kernel and the partial-tile traffic cost
+    // more than they save.
     if (best.variant == DG_VARIANT_MFMA && ws_bytes > 0 && p.K > 0) {
         const int64_t tiles = ((p.M + best.block_m - 1) / best.block_m) * ((p.N + best.block_n - 1) / best.block_n) * nb;
-        int64_t s = std::min<int64_t>({(int64_t)cus / std::max<int64_t>(tiles, 1), 16, p.K / (4 * best.block_k)});
+        int64_t s = (int64_t)cus / std::max<int64_t>(tiles, 1);
+        const int64_t lds = (int64_t)best.stages * (best.block_m + best.block_n) * best.block_k * 2;
+        if (p.K >= 8192 && tiles <= cus && 2 * lds <= 160 * 1024) s = std::max<int64_t>(s, 2);
+        s = std::min<int64_t>({s, 16, p.K / 1024});
         if (s >= 2) {
             dg_config c = best;
             c.k_splits = (int32_t)s;
@@ -497,10 +507,13 @@ dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream, voi
     g.bsa = p.bsa;
     g.bsb = p.bsb;
     g.bsc = p.bsc;
+    LaunchFn reduce = nullptr;
     if (sp.splits > 1) {
-        const WsLayout L = ws_layout(p.M, p.N, p.batch, cfg, sp.splits);
-        g.counters = static_cast<uint32_t *>(ws);
-        g.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + L.counters);
+        g.ws = static_cast<float *>(ws);
+        reduce = split_reduce_kernel(cfg.block_m, cfg.block_n, cfg.waves);
+        if (!reduce)
+            return fail(DG_ERR_NO_CONFIG, "no split-K reduction kernel for block %dx%d with %d waves", cfg.block_m,
+                        cfg.block_n, cfg.waves);
     }
     const Epi &ep = p.epi;
     g.epi = ep.general() ? 1 : 0;
@@ -528,8 +541,13 @@ dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream, voi
                               : nullptr;
         g.bias = ep.bias ? static_cast<const char *>(ep.bias) + (intptr_t)(b0 * p.bsbias * elem_size(ep.bias_dtype))
                          : nullptr;
-        const hipError_t err = e->launch(g, stream);
+        hipError_t err = e->launch(g, stream);
         if (err != hipSuccess) return fail(DG_ERR_HIP, "launch of %s failed: %s", e->name, hipGetErrorString(err));
+        if (reduce) {
+            err = reduce(g, stream);
+            if (err != hipSuccess)
+                return fail(DG_ERR_HIP, "launch of the split-K reduction failed: %s", hipGetErrorString(err));
+        }
     }
     return DG_OK;
 }
@@ -637,21 +655,31 @@ dg_status dg_validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t sa
     return validate(make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype));
 }
 
-dg_status dg_select_config(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
-                           int64_t sbk, int64_t sbn, const void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
-                           dg_dtype out_dtype, dg_config *out, int32_t *from_cache) {
+dg_status dg_select_config_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak,
+                              const void *B, int64_t sbk, int64_t sbn, const void *C, int64_t scm, int64_t scn,
+                              dg_dtype in_dtype, dg_dtype out_dtype, const dg_batch *batch, int64_t workspace_bytes,
+                              dg_config *out, int32_t *from_cache) {
     g_last_error.clear();
     if (!out) return fail(DG_ERR_INVALID_VALUE, "out is NULL");
+    if (workspace_bytes < 0) return fail(DG_ERR_INVALID_VALUE, "negative workspace size");
     // NULL pointers are inspected for alignment only: stand in an aligned address.
     static const char aligned_stub[16] __attribute__((aligned(16))) = {0};
     Problem p = make_problem(M, N, K, A ? A : aligned_stub, sam, sak, B ? B : aligned_stub, sbk, sbn,
                              C ? C : aligned_stub, scm, scn, in_dtype, out_dtype);
+    apply_ex(p, nullptr, batch);
     dg_status s = validate(p);
     if (s != DG_OK) return s;
     bool hit = false;
-    *out = choose(p, 0, &hit);
+    *out = choose(p, workspace_bytes, &hit);
     if (from_cache) *from_cache = hit ? 1 : 0;
     return DG_OK;
+}
+
+dg_status dg_select_config(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
+                           int64_t sbk, int64_t sbn, const void *C, int64_t scm, int64_t scn, dg_dtype in_dtype,
+                           dg_dtype out_dtype, dg_config *out, int32_t *from_cache) {
+    return dg_select_config_ex(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype, nullptr, 0, out,
+                               from_cache);
 }
 
 dg_status dg_gemm_config(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak, const void *B,
@@ -704,7 +732,7 @@ dg_status dg_gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam
 }
 
 dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count, const dg_config *cfg,
-                            int64_t *bytes, int64_t *counter_bytes) {
+                            int64_t *bytes) {
     g_last_error.clear();
     if (!cfg || !bytes) return fail(DG_ERR_INVALID_VALUE, "NULL argument");
     if (M < 0 || N < 0 || K < 0 || batch_count < 0) return fail(DG_ERR_INVALID_VALUE, "negative size");
@@ -713,7 +741,6 @@ dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count
     const WsLayout L = ws_layout(M, N, batch_count, *cfg, split_plan(K, *cfg).splits);
     if (L.total < 0) return fail(DG_ERR_UNSUPPORTED, "workspace size overflows");
     *bytes = L.total;
-    if (counter_bytes) *counter_bytes = L.counters;
     return DG_OK;
 }
 

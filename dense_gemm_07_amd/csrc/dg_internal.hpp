@@ -37,7 +37,6 @@ struct GemmArgs {
     int32_t k_chunk;        // K elements per range (a multiple of block_k when splits > 1)
     int64_t bsa, bsb, bsc;  // batch strides of A, B, C
     float *ws;              // split-K partial tiles (fp32)
-    uint32_t *counters;     // split-K arrival count per (product, tile); zero between launches
     // fused epilogue: C = act(alpha * acc + beta * R + bias)
     int32_t epi;            // 0: C = acc (the other fields are unused); 1: the general form
     int32_t act;            // dg_activation
@@ -78,6 +77,8 @@ struct KernelEntry {
 
 // Registration hooks, one per kernel translation unit.
 void register_simt(std::vector<KernelEntry> &out);
+// The split-K reduction kernel for an MFMA tile shape (nullptr if none).
+LaunchFn split_reduce_kernel(int block_m, int block_n, int waves);
 #define DG_DECLARE_MFMA_HOOKS(t)                               \
     void register_mfma_##t##_kc_rc(std::vector<KernelEntry> &out); \
     void register_mfma_##t##_kc_kc(std::vector<KernelEntry> &out); \
@@ -132,7 +133,8 @@ __host__ __device__ inline void tile_coords(int wg, int grid_m, int grid_n, int 
 }
 
 // What one workgroup of a launch computes: tile (pm, pn) of product `prod`,
-// K range `split`; `slot` numbers the (product, tile) pair. The XCD
+// K range `split`; `slot` = prod * tiles + pm * grid_n + pn numbers the
+// (product, tile) pair. The XCD
 // renumbering runs over all workgroups of the launch, so the ids one XCD
 // serves are consecutive tiles of one product and K range.
 struct WorkItem {
@@ -148,8 +150,8 @@ __host__ __device__ inline WorkItem work_item(int wg, const GemmArgs &g) {
     const int rest = lid / tiles;
     w.split = rest % g.splits;
     w.prod = rest / g.splits;
-    w.slot = w.prod * tiles + t;
     group_major(t, g.grid_m, g.grid_n, g.group_m, w.pm, w.pn);
+    w.slot = w.prod * tiles + w.pm * g.grid_n + w.pn;  // row-major tile number: independent of launch order
     return w;
 }
 

@@ -447,65 +447,35 @@ __device__ __forceinline__ void write_tile(const GemmArgs &g, const WorkItem &w,
     else store_acc<F32, FM, FN>(g, c_off, acc, row_base, col_base, interior);
 }
 
-// ---- split-K reduction ---------------------------------------------------------
+// ---- split-K -------------------------------------------------------------------
 // The K loop is cut into g.splits ranges, each run by its own workgroup
-// (more workgroups when a problem has few output tiles; latency is hidden
-// by having many programs in flight, "Triton：04 Matmul、Autotune 与 PyTorch
-// 集成"). Each workgroup stores its fp32 partial tile in the workspace,
-// publishes it (device-scope release), and counts its arrival on the tile's
-// counter. The workgroup that arrives last acquires, adds the partials in
-// range order 0, 1, ..., S-1 (the same order whichever arrives last, so the
-// result is deterministic), resets the counter for the next launch, and runs
-// the epilogue. No workgroup waits for another.
+// (more workgroups in flight when a problem has few output tiles; latency
+// is hidden by having many programs in flight, "Triton：04 Matmul、Autotune 与
+// PyTorch 集成"). Each workgroup stores its fp32 partial tile to the
+// workspace and exits; a second kernel (gemm_split_reduce, same tile shape
+// and thread layout) adds the partials of a tile in range order 0, 1, ...,
+// S-1 -- so the result does not depend on which range finished first -- and
+// runs the epilogue. The kernel boundary makes the partials visible to the
+// reducer on every XCD. (Doing the reduction in the last-arriving workgroup
+// instead needs device-scope release/acquire fences per workgroup, which
+// write back and invalidate the XCD's whole L2; measured, that made a
+// 1024^3 split 8x slower than no split.)
 //
 // Workspace layout of a partial: float4 v of thread t at [v * T + t], v over
-// (block i, block j, quarter q) = registers 4q..4q+3 of acc[i][j]; one slot of
-// S partials per (product, tile).
+// (block i, block j, quarter q) = registers 4q..4q+3 of acc[i][j]; the S
+// partials of one (product, tile) slot are consecutive.
 template <int FM, int FN, int T>
-__device__ __forceinline__ bool split_reduce(const GemmArgs &g, const WorkItem &w, f32x16 (&acc)[FM][FN],
-                                             uint32_t *flag) {
+__device__ __forceinline__ void split_store(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN]) {
     constexpr int V = FM * FN * 4;
-    const int tid = threadIdx.x;
-    float4 *slot = reinterpret_cast<float4 *>(g.ws) + (int64_t)w.slot * g.splits * (V * T);
-    float4 *mine = slot + (int64_t)w.split * (V * T);
+    float4 *mine = reinterpret_cast<float4 *>(g.ws) + ((int64_t)w.slot * g.splits + w.split) * (V * T);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                mine[((i * FN + j) * 4 + q) * T + tid] =
+                mine[((i * FN + j) * 4 + q) * T + threadIdx.x] =
                     make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-    __threadfence();  // this thread's partial is visible device-wide before the arrival is counted
-    __syncthreads();
-    if (tid == 0) *flag = atomicAdd(g.counters + w.slot, 1u) == (uint32_t)(g.splits - 1) ? 1u : 0u;
-    __syncthreads();
-    if (*flag == 0u) return false;
-    __threadfence();  // acquire: the other ranges' partials are visible
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int v = (i * FN + j) * 4 + q;
-                const float4 own = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                               acc[i][j][4 * q + 3]);
-                float4 sum = w.split == 0 ? own : slot[v * T + tid];
-                for (int s = 1; s < g.splits; ++s) {
-                    const float4 p = s == w.split ? own : slot[((int64_t)s * V + v) * T + tid];
-                    sum.x += p.x;
-                    sum.y += p.y;
-                    sum.z += p.z;
-                    sum.w += p.w;
-                }
-                acc[i][j][4 * q] = sum.x;
-                acc[i][j][4 * q + 1] = sum.y;
-                acc[i][j][4 * q + 2] = sum.z;
-                acc[i][j][4 * q + 3] = sum.w;
-            }
-    if (tid == 0) g.counters[w.slot] = 0u;
-    return true;
 }
 
 // WM x WN waves, each owning a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.
@@ -593,8 +563,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
         __syncthreads();
     }
 
-    // the split-K arrival flag reuses the LDS (the K loop ended with a barrier)
-    if (g.splits > 1 && !split_reduce<FM, FN, T>(g, w, acc, reinterpret_cast<uint32_t *>(&lds[0][0]))) return;
+    if (g.splits > 1) {  // partial tile to the workspace; gemm_split_reduce finishes it
+        split_store<FM, FN, T>(g, w, acc);
+        return;
+    }
 
     // Epilogue: fp32 accumulators -> C's dtype, masked to C's view.
     write_tile<BM, BN, WM, WN, FM, FN, (int)sizeof(lds)>(g, w, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0);
@@ -835,8 +807,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
 
     // One LDS object only: the compiler proves the fragment reads independent
     // of the in-flight LDS loads per object, and a second __shared__ variable
-    // makes it wait for every load before each read. The split-K arrival flag
-    // reuses the pipeline's LDS once the K loop is done.
+    // makes it wait for every load before each read. The epilogue reuses this
+    // LDS once the K loop is done.
     __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
     const WorkItem w = work_item(blockIdx.x, g);
@@ -945,9 +917,60 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     }
     wait_vmcnt<0>();  // the out-of-range tail loads must land before the workgroup can exit
 
-    if (g.splits > 1 && !split_reduce<FM, FN, NW * 64>(g, w, acc, reinterpret_cast<uint32_t *>(lds))) return;
+    if (g.splits > 1) {  // partial tile to the workspace; gemm_split_reduce finishes it
+        split_store<FM, FN, NW * 64>(g, w, acc);
+        return;
+    }
 
     write_tile<BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
+}
+
+// ============================================================================
+// gemm_split_reduce: the second half of split-K
+// ============================================================================
+// One workgroup per (product, tile), the thread layout of the MFMA kernel that
+// wrote the partials (WM x WN waves): thread t sums its float4s over the
+// ranges in order 0..S-1 and holds the result in the accumulator layout, so
+// the epilogue is the MFMA kernels' own write_tile.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_split_reduce(GemmArgs g) {
+    constexpr int T = WM * WN * 64;
+    constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+    constexpr int V = FM * FN * 4;
+    constexpr int CAP = 64 * 1024;  // epilogue staging: at least 32 rows of every tile width
+    __shared__ __attribute__((aligned(16))) float st[CAP / 4];
+
+    const int tiles = g.grid_m * g.grid_n;
+    WorkItem w;
+    w.slot = blockIdx.x;
+    w.prod = w.slot / tiles;
+    w.split = 0;
+    const int t = w.slot - w.prod * tiles;
+    w.pm = t / g.grid_n;
+    w.pn = t - w.pm * g.grid_n;
+    const float4 *slot = reinterpret_cast<const float4 *>(g.ws) + (int64_t)w.slot * g.splits * (V * T);
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int v = (i * FN + j) * 4 + q;
+                float4 sum = slot[v * T + threadIdx.x];
+                for (int s = 1; s < g.splits; ++s) {
+                    const float4 p = slot[((int64_t)s * V + v) * T + threadIdx.x];
+                    sum.x += p.x;
+                    sum.y += p.y;
+                    sum.z += p.z;
+                    sum.w += p.w;
+                }
+                acc[i][j][4 * q] = sum.x;
+                acc[i][j][4 * q + 1] = sum.y;
+                acc[i][j][4 * q + 2] = sum.z;
+                acc[i][j][4 * q + 3] = sum.w;
+            }
+    write_tile<BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, w.pm * BM, w.pn * BN);
 }
 
 }  // namespace dg

@@ -89,9 +89,10 @@ enum {
  *             (one L2) are consecutive in the group-major order.
  *  k_splits:  1 (or 0) = one workgroup walks all of K for its tile; S > 1 =
  *             split-K: S workgroups per tile each walk one K range of
- *             block_k-multiple length and the last to finish sums the S fp32
- *             partials in split order (deterministic) before the epilogue.
- *             Needs a workspace (dg_gemm_ex); MFMA kernels only.
+ *             block_k-multiple length and store an fp32 partial tile; a
+ *             second kernel sums the partials in range order (deterministic)
+ *             and runs the epilogue. Needs a workspace (dg_gemm_ex); MFMA
+ *             kernels only.
  */
 typedef struct dg_config {
     int32_t block_m, block_n, block_k;
@@ -213,14 +214,15 @@ typedef struct dg_batch {
  * epilogue, an optional strided batch, an optional explicit config (NULL:
  * the library's choice, as dg_gemm) and an optional workspace.
  *
- * workspace / workspace_bytes: DEVICE memory, 256-byte aligned, that the
- * kernels use for split-K (config k_splits > 1, see dg_workspace_size).
- * NULL / 0 if none. With cfg == NULL and a workspace, the library may choose
- * split-K for problems with few output tiles when the workspace is large
- * enough; without one it never splits. The leading counter bytes of the
- * workspace (dg_workspace_size) must be zero before the first call that
- * uses it (a zero-filled allocation); each call leaves them zero again when
- * it completes. Calls that share a workspace must not run concurrently
+ * workspace / workspace_bytes: DEVICE memory, 256-byte aligned, for split-K
+ * (config k_splits > 1; size from dg_workspace_size). NULL / 0 if none.
+ * With cfg == NULL and a workspace, the library may choose split-K for
+ * problems whose output tiles leave most of the GPU idle and whose K is long,
+ * when the workspace is large enough; without one it never splits. Split-K
+ * runs as two kernels on `stream`: the K ranges store fp32 partial tiles in
+ * the workspace, then a reduction kernel adds each tile's partials in range
+ * order (deterministic) and applies the epilogue. The workspace needs no
+ * initialisation. Calls that share a workspace must not run concurrently
  * (issue them on one stream, or synchronise). The library never allocates.
  * An explicit config with k_splits > 1 and no (or too small a) workspace is
  * DG_ERR_INVALID_VALUE; with a SIMT config it is DG_ERR_NO_CONFIG.
@@ -253,14 +255,14 @@ dg_status dg_autotune_ex(int64_t M, int64_t N, int64_t K,
 
 /*
  * Workspace bytes config `cfg` needs for an M x N x K problem with
- * `batch_count` products: 0 when it does not split K. *counter_bytes (may be
- * NULL) receives the size of the leading counter region that must start
- * zeroed. K is cut into ranges of k_chunk = block_k * ceil(ceil(K /
- * k_splits) / block_k) elements; the ranges actually used number
- * ceil(K / k_chunk) (at most k_splits; 1 when K <= block_k).
+ * `batch_count` products: 0 when it does not split K, else one fp32 partial
+ * tile per (product, tile, K range) = tiles * batch_count * ranges *
+ * block_m * block_n * 4. K is cut into ranges of k_chunk = block_k *
+ * ceil(ceil(K / k_splits) / block_k) elements; the ranges actually used
+ * number ceil(K / k_chunk) (at most k_splits; 1 when K <= block_k).
  */
 dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count, const dg_config *cfg,
-                            int64_t *bytes, int64_t *counter_bytes);
+                            int64_t *bytes);
 
 /*
  * The config dg_gemm would use, without any GPU work. The pointers are only
@@ -275,6 +277,18 @@ dg_status dg_select_config(int64_t M, int64_t N, int64_t K,
                            const void *C, int64_t stride_cm, int64_t stride_cn,
                            dg_dtype in_dtype, dg_dtype out_dtype,
                            dg_config *out, int32_t *from_cache);
+
+/*
+ * The config dg_gemm_ex would use with cfg == NULL for this batch (NULL: one
+ * product) and a workspace of workspace_bytes (split-K is chosen only when
+ * its workspace fits), without any GPU work. Pointers as dg_select_config.
+ */
+dg_status dg_select_config_ex(int64_t M, int64_t N, int64_t K,
+                              const void *A, int64_t stride_am, int64_t stride_ak,
+                              const void *B, int64_t stride_bk, int64_t stride_bn,
+                              const void *C, int64_t stride_cm, int64_t stride_cn,
+                              dg_dtype in_dtype, dg_dtype out_dtype, const dg_batch *batch,
+                              int64_t workspace_bytes, dg_config *out, int32_t *from_cache);
 
 /* Autotune candidates for a dtype pair: count, and the i-th (0-based). */
 int32_t dg_num_candidates(dg_dtype in_dtype, dg_dtype out_dtype);

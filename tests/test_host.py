@@ -271,7 +271,7 @@ def test_gemm_ex_split_k_argument_errors():
     assert gemm_ex_status(K=4096, cfg=cfg) == INVALID
     assert b"workspace" in dg.library().dg_last_error()
     assert gemm_ex_status(K=4096, cfg=cfg, ws=FAKE, ws_bytes=1024) == INVALID
-    need = dg.workspace_size(64, 64, 4096, 1, cfg)[0]
+    need = dg.workspace_size(64, 64, 4096, 1, cfg)
     assert gemm_ex_status(K=4096, cfg=cfg, ws=FAKE + 16, ws_bytes=need) == INVALID
     assert gemm_ex_status(K=4096, cfg=cfg, ws=FAKE, ws_bytes=-5) == INVALID
     # split-K is an MFMA feature
@@ -282,17 +282,17 @@ def test_gemm_ex_split_k_argument_errors():
 
 def test_workspace_size_arithmetic():
     cfg = mfma_cfg(128, 128, 64, splits=4)
-    # 8 x 8 tiles, K ranges of 256: 4 ranges; counters 64*4 B padded to 256
-    assert dg.workspace_size(1024, 1024, 1024, 1, cfg) == (256 + 64 * 4 * 128 * 128 * 4, 256)
-    # batch multiplies tiles; counters 3*64*4 = 768 B
-    assert dg.workspace_size(1024, 1024, 1024, 3, cfg) == (768 + 3 * 64 * 4 * 128 * 128 * 4, 768)
+    # 8 x 8 tiles, K ranges of 256: 4 ranges
+    assert dg.workspace_size(1024, 1024, 1024, 1, cfg) == 64 * 4 * 128 * 128 * 4
+    # batch multiplies tiles
+    assert dg.workspace_size(1024, 1024, 1024, 3, cfg) == 3 * 64 * 4 * 128 * 128 * 4
     # K = 200, 3 requested: chunks of ceil(67/64)*64 = 128 -> 2 ranges
     cfg3 = mfma_cfg(128, 128, 64, splits=3)
-    assert dg.workspace_size(128, 128, 200, 1, cfg3) == (256 + 2 * 128 * 128 * 4, 256)
+    assert dg.workspace_size(128, 128, 200, 1, cfg3) == 2 * 128 * 128 * 4
     # one K slice or no split: nothing
-    assert dg.workspace_size(1024, 1024, 64, 1, cfg) == (0, 0)
-    assert dg.workspace_size(1024, 1024, 4096, 1, mfma_cfg(splits=1)) == (0, 0)
-    assert dg.workspace_size(0, 1024, 4096, 1, cfg) == (0, 0)
+    assert dg.workspace_size(1024, 1024, 64, 1, cfg) == 0
+    assert dg.workspace_size(1024, 1024, 4096, 1, mfma_cfg(splits=1)) == 0
+    assert dg.workspace_size(0, 1024, 4096, 1, cfg) == 0
 
 
 def test_select_config_never_splits_without_workspace():
@@ -307,3 +307,22 @@ def test_autotune_ex_rejects_epilogue_reading_c():
     st = lib.dg_autotune_ex(64, 64, 64, FAKE, 64, 1, FAKE, 64, 1, FAKE, 64, 1, BF16, BF16, None,
                             ctypes.byref(epi), None, None, 0, 1, None, None)
     assert st == INVALID and b"reads C" in lib.dg_last_error()
+
+
+def test_gemm_ex_default_split_choice():
+    """Split counts the library picks for dg_gemm_ex with a workspace (the measured rule)."""
+    cases = {(1024, 1024, 1024): 1, (1, 14336, 4096): 1, (512, 512, 4096): 4, (256, 256, 32768): 16,
+             (2048, 512, 8192): 2, (128, 128, 8192): 8, (64, 64, 65536): 16}
+    for (M, N, K), want in cases.items():
+        c, _ = dg.select_config_ex(M, N, K, (K, 1), (N, 1), (N, 1), BF16, BF16, batch=1,
+                                   workspace_bytes=1 << 30)
+        assert (c.block_m, c.k_splits) == (64, want), ((M, N, K), c)
+        assert dg.workspace_size(M, N, K, 1, c) <= 1 << 30
+    # no (or too small a) workspace: never split
+    c, _ = dg.select_config_ex(256, 256, 32768, (32768, 1), (256, 1), (256, 1), BF16, BF16, batch=1,
+                               workspace_bytes=1024)
+    assert c.k_splits == 1
+    # a batch that fills the GPU needs no split
+    c, _ = dg.select_config_ex(256, 256, 32768, (32768, 1), (256, 1), (256, 1), BF16, BF16, batch=64,
+                               workspace_bytes=1 << 30)
+    assert c.k_splits == 1
