@@ -134,6 +134,12 @@ def main():
                     help="no GPU work: turn rocprofv3 counter CSVs into profiles/traffic_<workload>.json")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (with --record-traffic)")
     ap.add_argument("--commands", default="", help="commands that produced the CSVs (with --record-traffic)")
+    ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias_relu", "bias_gelu", "residual"],
+                    help="time dg_gemm_ex with a fused epilogue: fp32 bias per column (+ activation), or "
+                         "C = A@B + R with a separate residual R of C's dtype")
+    ap.add_argument("--batch", type=int, default=1, help="time a strided batch of this many products (dg_gemm_ex)")
+    ap.add_argument("--split-k", action="store_true",
+                    help="time dg_gemm_ex with a workspace (the library may split K)")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(args.workload, *args.record_traffic, args.copy_mib, args.commands)
@@ -160,42 +166,78 @@ def main():
         return
     if not os.path.exists(LIB):
         build()
-    w = inputs.WORKLOADS.get(args.workload) or inputs.SKINNY[args.workload]
+    w = inputs.find(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    a_cpu, b_cpu = inputs.make(w, seed=0)
-    a = inputs.to_device_like(a_cpu, dev)
-    b = inputs.to_device_like(b_cpu, dev)
-    c = torch.empty((w.M, w.N), dtype=inputs.TORCH_DTYPES[w.out_dtype], device=dev)
+    nb = max(1, args.batch)
+    ex = args.epilogue != "none" or nb > 1 or args.split_k
+    out_dt = inputs.TORCH_DTYPES[w.out_dtype]
+    if nb > 1:
+        a_cpu, b_cpu = inputs.make_batch(w, nb, seed=0)
+        a, b = a_cpu.to(dev), b_cpu.to(dev)
+        c = torch.empty((nb, w.M, w.N), dtype=out_dt, device=dev)
+    else:
+        a_cpu, b_cpu = inputs.make(w, seed=0)
+        a = inputs.to_device_like(a_cpu, dev)
+        b = inputs.to_device_like(b_cpu, dev)
+        c = torch.empty((w.M, w.N), dtype=out_dt, device=dev)
+    # Epilogue operands (seeded): an fp32 bias per column, or a residual of C's dtype.
+    gen = torch.Generator().manual_seed(1)
+    epi = {}
+    extra_bytes = 0
+    if args.epilogue.startswith("bias"):
+        epi["bias"] = torch.randn((nb, w.N) if nb > 1 else (w.N,), generator=gen).to(dev)
+        epi["activation"] = {"bias": None, "bias_relu": "relu", "bias_gelu": "gelu"}[args.epilogue]
+        extra_bytes = 4 * w.N * nb
+    elif args.epilogue == "residual":
+        epi["residual"] = torch.randn(c.shape, generator=gen).to(out_dt).to(dev)
+        epi["beta"] = 1.0
+        extra_bytes = c.numel() * c.element_size()
     torch.cuda.synchronize()
 
     tune_s = 0.0
-    if args.autotune and not args.no_autotune:
+    if args.autotune and not args.no_autotune and not ex:
         t0 = time.perf_counter()
         cfg, _ = dg.autotune(a, b, out=c, repeats=10)
         tune_s = time.perf_counter() - t0
-    cfg, _ = dg.select_config(a, b, c)
+    if ex:
+        ws_bytes = dg.DEFAULT_WORKSPACE_BYTES if args.split_k else 0
+        cfg, _ = dg.select_config_ex(w.M, w.N, w.K, a.stride()[-2:], b.stride()[-2:], c.stride()[-2:],
+                                     dg._dtype_code(a.dtype), dg._dtype_code(c.dtype), batch=nb,
+                                     workspace_bytes=ws_bytes, ptr_a=a.data_ptr(), ptr_b=b.data_ptr(),
+                                     ptr_c=c.data_ptr(),
+                                     batch_strides=(a.stride(0), b.stride(0), c.stride(0)) if nb > 1 else (0, 0, 0))
+    else:
+        cfg, _ = dg.select_config(a, b, c)
     print(f"# workload {w.name}: config {cfg} (autotune {tune_s:.2f} s)", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
+    if ex:
+        def step():
+            dg.gemm_ex(a, b, out=c, stream=stream, workspace=True if args.split_k else None, **epi)
+    else:
+        def step():
+            dg.gemm(a, b, out=c, stream=stream)
     for _ in range(args.warmup):
-        dg.gemm(a, b, out=c, stream=stream)
+        step()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
-        dg.gemm(a, b, out=c, stream=stream)
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    tflops = w.flops / (ms * 1e-3) / 1e12
+    flops = w.flops * nb
+    nbytes = w.compulsory_bytes() * nb + extra_bytes
+    tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.in_dtype]
-    traffic = measured_traffic(w.name)
-    hbm_bound = w.flops / w.compulsory_bytes() < peak * 1e12 / (HBM_GBPS * 1e9)
+    traffic = measured_traffic(w.name) if not ex else None
+    hbm_bound = flops / nbytes < peak * 1e12 / (HBM_GBPS * 1e9)
     if hbm_bound:  # below the ridge: algorithmic bytes over time against the HBM peak
-        gbps = w.compulsory_bytes() / (ms * 1e-3) / 1e9
+        gbps = nbytes / (ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
                     "frac": round(gbps / HBM_GBPS, 4), "traffic": traffic}
     else:
@@ -220,7 +262,9 @@ def main():
                    "kernel_config": cfg.as_dict(), "autotune_s": round(tune_s, 3)},
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if ex:
+        result["config"].update({"epilogue": args.epilogue, "batch": nb, "split_k_allowed": args.split_k})
+    if not args.no_cpu_baseline and not ex:
         result["cpu_baseline"] = cpu_baseline(w, a_cpu, b_cpu)
     print(json.dumps(result), flush=True)
 

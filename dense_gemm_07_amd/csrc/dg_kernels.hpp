@@ -69,12 +69,46 @@ __device__ __forceinline__ float load_any(const void *p, int64_t off, int dt) {
     return static_cast<const float *>(p)[off];
 }
 
-// ReLU keeps NaN and -0 (only v < 0 becomes +0). GELU is v * Phi(v) with the
-// normal CDF written through erfc, which stays accurate for large negative
-// v where 1 + erf(v / sqrt 2) would cancel.
+// Upper tail of the standard normal, Q(x) = Phi(-x), for x >= 0:
+// exp(-x^2/2) * t * P(t) with t = 1 / (1 + 0.3 x) and P of degree 9, fitted
+// to 3.5e-9 relative error on [0, 14] (fit_normal_tail.py). x^2 is carried
+// as hi + lo so the exponent is exact to fp32 rounding; no branches, so a
+// wave whose lanes fall in different ranges runs it once. Measured end to
+// end in fp32 emulation: <= 7 ulp relative where the result is normal.
+__device__ __forceinline__ float normal_tail(float x) {
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3f * x);  // hardware reciprocal, 1 ulp
+    float p = -0.0206153598f;
+    p = __builtin_fmaf(p, t, 0.11239133f);
+    p = __builtin_fmaf(p, t, -0.228108361f);
+    p = __builtin_fmaf(p, t, 0.191641822f);
+    p = __builtin_fmaf(p, t, -0.0793019533f);
+    p = __builtin_fmaf(p, t, 0.0960895121f);
+    p = __builtin_fmaf(p, t, 0.0784138665f);
+    p = __builtin_fmaf(p, t, 0.110229976f);
+    p = __builtin_fmaf(p, t, 0.119572505f);
+    p = __builtin_fmaf(p, t, 0.119686648f);
+    // exp(-x^2/2) = 2^(-x^2 log2(e) / 2) with the exponent carried as
+    // a_hi + a_lo (x^2 = hi + lo exactly, and the product by log2(e)/2 keeps
+    // its rounding error), so v_exp_f32 sees an argument exact to fp32.
+    const float hi = x * x;
+    const float lo = __builtin_fmaf(x, x, -hi);
+    constexpr float kL = -0.72134752044448170368f;  // -log2(e) / 2
+    const float a_hi = hi * kL;
+    const float a_lo = __builtin_fmaf(hi, kL, -a_hi) + lo * kL;
+    const float e = __builtin_amdgcn_exp2f(a_hi) * __builtin_fmaf(a_lo, 0.69314718055994530942f, 1.0f);
+    return e * t * p;
+}
+
+// ReLU keeps NaN and -0 (only v < 0 becomes +0). GELU is v * Phi(v), with
+// Phi(v) = 1 - Q(v) for v >= 0 and Q(-v) below: no cancellation for large
+// negative v. |v| is clamped at 30, where Q is exactly 0 in fp32, so
+// GELU(+inf) = +inf and GELU(-inf) = -inf * 0 = NaN (the limit form's value).
 __device__ __forceinline__ float activate(float v, int act) {
     if (act == DG_ACT_RELU) return v < 0.0f ? 0.0f : v;
-    if (act == DG_ACT_GELU) return 0.5f * v * erfcf(-v * 0.70710678118654752440f);
+    if (act == DG_ACT_GELU) {
+        const float q = normal_tail(fminf(fabsf(v), 30.0f));
+        return v * (v >= 0.0f ? 1.0f - q : q);
+    }
     return v;
 }
 
@@ -373,14 +407,136 @@ __device__ __forceinline__ void store_acc(const GemmArgs &g, int64_t c_off, cons
     }
 }
 
-// The same tile through the fused epilogue, staged through LDS: the tile is
+// Four consecutive elements p[off .. off+3] (element stride 1) of dtype dt
+// as fp32, in one vector load when `vec` (the caller checked 4-element
+// alignment), else element by element for the first n (n <= 4) of them.
+__device__ __forceinline__ void load4(const void *p, int64_t off, int dt, bool vec, int n, float (&out)[4]) {
+    if (dt == DG_F32) {
+        const float *q = static_cast<const float *>(p) + off;
+        if (vec) {
+            const float4 v = *reinterpret_cast<const float4 *>(q);
+            out[0] = v.x, out[1] = v.y, out[2] = v.z, out[3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = e < n ? q[e] : 0.0f;
+        }
+        return;
+    }
+    const uint16_t *q = static_cast<const uint16_t *>(p) + off;
+    uint16_t h[4];
+    if (vec) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(q);
+        h[0] = (uint16_t)v.x, h[1] = (uint16_t)(v.x >> 16), h[2] = (uint16_t)v.y, h[3] = (uint16_t)(v.y >> 16);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = e < n ? q[e] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = dt == DG_BF16 ? to_f32<BF16>(h[e]) : to_f32<F16>(h[e]);
+}
+
+// Per-thread view of the staged tile for the fused epilogue: one 4-column
+// group (columns gn0 .. gn0+3 of C, ncols of them inside C) and the uniform
+// operands, decided once per tile.
+struct EpiRows {
+    const float *st;         // staged rows (LDS), row pitch ldn floats
+    int ldn, c4, r0, rs;     // this thread's column group in the tile, first row, row step
+    int m_row0;              // C row of staged row 0
+    int rows;                // staged rows inside C
+    int gn0, ncols;
+    char *C;                 // C of this product (bytes)
+    int c_es;
+    bool cvec, rvec, use_r;
+    int64_t r_off, b_off;
+    float bcol[4];           // per-column bias of the group (0 if none)
+    bool row_bias;
+};
+
+// Rounds and stores 4 values of one row (dtype OUT), vector store when vec.
+template <int OUT>
+__device__ __forceinline__ void store4_t(char *p, bool vec, int n, int64_t s, const float (&y)[4]) {
+    if constexpr (OUT == DG_F32) {
+        float *q = reinterpret_cast<float *>(p);
+        if (vec) {
+            *reinterpret_cast<float4 *>(q) = make_float4(y[0], y[1], y[2], y[3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < n) q[e * s] = y[e];
+        }
+    } else {
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = OUT == DG_BF16 ? from_f32<BF16>(y[e]) : from_f32<F16>(y[e]);
+        uint16_t *q = reinterpret_cast<uint16_t *>(p);
+        if (vec) {
+            *reinterpret_cast<uint2 *>(q) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                       (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < n) q[e * s] = h[e];
+        }
+    }
+}
+
+// The staged rows of one pass through act(alpha*x + beta*R + bias), for one
+// activation and output dtype (so the per-element work has no branches: an
+// absent residual or bias enters as +0, which changes at most the sign of a
+// zero result). The residual and per-row bias loads of U rows are issued
+// before any of them is used: the loop is otherwise bound by their latency.
+template <int ACT, int OUT, int U>
+__device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e) {
+#pragma unroll 1
+    for (int rr = e.r0; rr < e.rows; rr += U * e.rs) {
+        float rv[U][4], br[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // issue the global loads of U rows first
+            const int row = rr + u * e.rs;
+            const bool in = row < e.rows;
+            const int gm = e.m_row0 + row;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rv[u][k] = 0.0f;
+            if (in && e.use_r) {
+                const int64_t off = e.r_off + (int64_t)gm * g.srm;
+                if (g.srn == 1) {
+                    load4(g.R, off + e.gn0, g.r_dtype, e.rvec, e.ncols, rv[u]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (k < e.ncols) rv[u][k] = load_any(g.R, off + (int64_t)(e.gn0 + k) * g.srn, g.r_dtype);
+                }
+            }
+            br[u] = (in && e.row_bias) ? load_any(g.bias, e.b_off + (int64_t)gm * g.sbias, g.bias_dtype) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = rr + u * e.rs;
+            if (row >= e.rows) continue;
+            const float4 v = *reinterpret_cast<const float4 *>(e.st + row * e.ldn + e.c4);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+            float y[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float t = __builtin_fmaf(g.beta, rv[u][k], g.alpha * x[k]) + (e.bcol[k] + br[u]);
+                if constexpr (ACT == DG_ACT_RELU) t = t < 0.0f ? 0.0f : t;
+                if constexpr (ACT == DG_ACT_GELU) t = activate(t, DG_ACT_GELU);
+                y[k] = t;
+            }
+            store4_t<OUT>(e.C + ((int64_t)(e.m_row0 + row) * g.scm + (int64_t)e.gn0 * g.scn) * e.c_es, e.cvec,
+                          e.ncols, g.scn, y);
+        }
+    }
+}
+
+// The same tile through the fused epilogue, staged through LDS. The tile is
 // written to LDS (fp32, rows padded by 4 floats) in passes of whole 32-row
-// fragment blocks, then every thread walks the staged rows in row-major
-// order, so the residual reads and the C writes of a wave cover whole row
-// segments, and the per-element work is a compact loop instead of a fully
-// unrolled one per accumulator register. `st` is the kernel's LDS (CAP
-// bytes, free: the caller has finished the K loop).
-template <typename TO, int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
+// fragment blocks. Each thread then owns one 4-column group of the tile
+// (T is a multiple of BN/4) and walks its rows (epi_rows): a per-column bias
+// is loaded once per tile, and a row's 4 elements of C and of the residual
+// move as one vector when the layout allows. `st` is the kernel's LDS (CAP
+// bytes, free: the K loop is done).
+template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
 __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
                                           float *st, int m0, int n0) {
     constexpr int T = WM * WN * 64;
@@ -390,10 +546,38 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
     constexpr int PR = FIT >= BM ? BM : (FIT / 32) * 32;  // rows per pass
     static_assert(PR >= 32, "LDS too small to stage 32 rows of the tile");
     constexpr int Q = BN / 4;  // 4-column groups per row
+    static_assert(T % Q == 0, "every thread keeps one column group");
+    // Rows whose loads are in flight together: 8 where registers allow; 4
+    // for the large tiles, whose 128 accumulators would otherwise push the
+    // register count up enough to change how the K loop is scheduled.
+    constexpr int U = FM * FN >= 8 ? 4 : 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    typename TO::storage *C = static_cast<typename TO::storage *>(g.C) + (int64_t)w.prod * g.bsc;
-    const int64_t r_off = (int64_t)w.prod * g.bsr, b_off = (int64_t)w.prod * g.bsbias;
+    EpiRows e;
+    e.st = st;
+    e.ldn = LDN;
+    e.c4 = (tid % Q) * 4;
+    e.r0 = tid / Q;
+    e.rs = T / Q;
+    e.gn0 = n0 + e.c4;
+    e.ncols = min(4, g.N - e.gn0);
+    e.c_es = g.out_dtype == DG_F32 ? 4 : 2;
+    e.C = static_cast<char *>(g.C) + (int64_t)w.prod * g.bsc * e.c_es;
+    e.use_r = g.beta != 0.0f;
+    e.r_off = (int64_t)w.prod * g.bsr;
+    e.b_off = (int64_t)w.prod * g.bsbias;
+    e.row_bias = g.bias != nullptr && g.bias_per_row;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        e.bcol[k] = (g.bias != nullptr && !g.bias_per_row && k < e.ncols)
+                        ? load_any(g.bias, e.b_off + (int64_t)(e.gn0 + k) * g.sbias, g.bias_dtype)
+                        : 0.0f;
+    const int r_es = g.r_dtype == DG_F32 ? 4 : 2;
+    e.cvec = e.ncols == 4 && g.scn == 1 && g.scm % 4 == 0 &&
+             ((uintptr_t)(e.C + (int64_t)e.gn0 * e.c_es) % (uintptr_t)(4 * e.c_es)) == 0;
+    e.rvec = e.ncols == 4 && e.use_r && g.srn == 1 && g.srm % 4 == 0 &&
+             ((uintptr_t)g.R + (uintptr_t)((e.r_off + e.gn0) * r_es)) % (uintptr_t)(4 * r_es) == 0;
+#pragma unroll 1
     for (int p0 = 0; p0 < BM; p0 += PR) {
         __syncthreads();  // the previous pass (or the K loop) is done with the LDS
 #pragma unroll
@@ -409,42 +593,24 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
             }
         }
         __syncthreads();
-        const int rows = min(PR, g.M - m0 - p0);
-        for (int q = tid; q < rows * Q; q += T) {
-            const int row = q / Q, c4 = (q % Q) * 4;
-            const int gm = m0 + p0 + row;
-            const float4 v = *reinterpret_cast<const float4 *>(st + row * LDN + c4);
-            const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int gn = n0 + c4 + u;
-                if (gn < g.N)
-                    C[(int64_t)gm * g.scm + (int64_t)gn * g.scn] = from_f32<TO>(epilogue_value(g, e[u], gm, gn, r_off, b_off));
-            }
+        e.m_row0 = m0 + p0;
+        e.rows = min(PR, g.M - m0 - p0);
+        if (e.ncols <= 0) continue;
+        const int out = g.out_dtype;
+        if (g.act == DG_ACT_GELU) {
+            if (out == DG_BF16) epi_rows<DG_ACT_GELU, DG_BF16, U>(g, e);
+            else if (out == DG_F16) epi_rows<DG_ACT_GELU, DG_F16, U>(g, e);
+            else epi_rows<DG_ACT_GELU, DG_F32, U>(g, e);
+        } else if (g.act == DG_ACT_RELU) {
+            if (out == DG_BF16) epi_rows<DG_ACT_RELU, DG_BF16, U>(g, e);
+            else if (out == DG_F16) epi_rows<DG_ACT_RELU, DG_F16, U>(g, e);
+            else epi_rows<DG_ACT_RELU, DG_F32, U>(g, e);
+        } else {
+            if (out == DG_BF16) epi_rows<DG_ACT_NONE, DG_BF16, U>(g, e);
+            else if (out == DG_F16) epi_rows<DG_ACT_NONE, DG_F16, U>(g, e);
+            else epi_rows<DG_ACT_NONE, DG_F32, U>(g, e);
         }
     }
-}
-
-// Epilogue of the MFMA kernels: plain stores straight from the accumulator
-// registers, or the fused epilogue through LDS.
-template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
-__device__ __forceinline__ void write_tile(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
-                                           float *st, int m0, int n0) {
-    if (g.epi) {
-        if (g.out_dtype == DG_BF16) store_epi<BF16, BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
-        else if (g.out_dtype == DG_F16) store_epi<F16, BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
-        else store_epi<F32, BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
-        return;
-    }
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row_base = m0 + (wave / WN) * WTM + 4 * (lane >> 5);
-    const int col_base = n0 + (wave % WN) * WTN + (lane & 31);
-    const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
-    const int64_t c_off = (int64_t)w.prod * g.bsc;
-    if (g.out_dtype == DG_BF16) store_acc<BF16, FM, FN>(g, c_off, acc, row_base, col_base, interior);
-    else if (g.out_dtype == DG_F16) store_acc<F16, FM, FN>(g, c_off, acc, row_base, col_base, interior);
-    else store_acc<F32, FM, FN>(g, c_off, acc, row_base, col_base, interior);
 }
 
 // ---- split-K -------------------------------------------------------------------
@@ -478,8 +644,47 @@ __device__ __forceinline__ void split_store(const GemmArgs &g, const WorkItem &w
                     make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
 }
 
+// How a kernel instantiation finishes its tile. Each MFMA kernel is compiled
+// once per mode and the launcher picks the instantiation from the
+// arguments: the fused epilogue's registers and code would otherwise change
+// how the compiler schedules the K loop of the plain kernel (measured: 9%
+// slower at 4096^3).
+enum EpiMode : int { EM_STORE = 0, EM_FUSED = 1, EM_SPLIT = 2 };
+
+// Plain stores straight from the accumulator registers.
+template <int BM, int BN, int WM, int WN, int FM, int FN>
+__device__ __forceinline__ void write_plain(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
+                                            int m0, int n0) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row_base = m0 + (wave / WN) * WTM + 4 * (lane >> 5);
+    const int col_base = n0 + (wave % WN) * WTN + (lane & 31);
+    const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
+    const int64_t c_off = (int64_t)w.prod * g.bsc;
+    if (g.out_dtype == DG_BF16) store_acc<BF16, FM, FN>(g, c_off, acc, row_base, col_base, interior);
+    else if (g.out_dtype == DG_F16) store_acc<F16, FM, FN>(g, c_off, acc, row_base, col_base, interior);
+    else store_acc<F32, FM, FN>(g, c_off, acc, row_base, col_base, interior);
+}
+
+// Either epilogue, chosen at run time (the split-K reduction kernel).
+template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
+__device__ __forceinline__ void write_tile(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
+                                           float *st, int m0, int n0) {
+    if (g.epi) store_epi<BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
+    else write_plain<BM, BN, WM, WN, FM, FN>(g, w, acc, m0, n0);
+}
+
+// The end of an MFMA kernel in mode EM.
+template <int EM, int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
+__device__ __forceinline__ void finish_tile(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
+                                            float *st, int m0, int n0) {
+    if constexpr (EM == EM_SPLIT) split_store<FM, FN, WM * WN * 64>(g, w, acc);  // gemm_split_reduce finishes it
+    else if constexpr (EM == EM_FUSED) store_epi<BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
+    else write_plain<BM, BN, WM, WN, FM, FN>(g, w, acc, m0, n0);
+}
+
 // WM x WN waves, each owning a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.
-template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB>
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int EM>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
     constexpr int T = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -563,13 +768,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
         __syncthreads();
     }
 
-    if (g.splits > 1) {  // partial tile to the workspace; gemm_split_reduce finishes it
-        split_store<FM, FN, T>(g, w, acc);
-        return;
-    }
-
     // Epilogue: fp32 accumulators -> C's dtype, masked to C's view.
-    write_tile<BM, BN, WM, WN, FM, FN, (int)sizeof(lds)>(g, w, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0);
+    finish_tile<EM, BM, BN, WM, WN, FM, FN, (int)sizeof(lds)>(g, w, acc, reinterpret_cast<float *>(&lds[0][0]), m0,
+                                                              n0);
 }
 
 // ============================================================================
@@ -795,7 +996,7 @@ __device__ __forceinline__ void interleave_mfma() {
 // kt-1 used, then multiplies slice kt. Slices past K are queued as
 // out-of-range loads (zeros into a free buffer) so that every step issues the
 // same number of loads and the wait count stays a constant.
-template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S, int EM>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -917,12 +1118,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     }
     wait_vmcnt<0>();  // the out-of-range tail loads must land before the workgroup can exit
 
-    if (g.splits > 1) {  // partial tile to the workspace; gemm_split_reduce finishes it
-        split_store<FM, FN, NW * 64>(g, w, acc);
-        return;
-    }
-
-    write_tile<BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
+    finish_tile<EM, BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
 }
 
 // ============================================================================

@@ -12,14 +12,23 @@ constexpr bool direct_to_lds() {
     return (LA == LD_KC || LA == LD_RC) && (LB == LD_KC || LB == LD_RC);
 }
 
-template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
-hipError_t launch_mfma(const GemmArgs &g, hipStream_t s) {
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S, int EM>
+void launch_mode(const GemmArgs &g, hipStream_t s) {
     const unsigned groups = launch_groups(g);
     if constexpr (direct_to_lds<LA, LB>())
-        hipLaunchKernelGGL((gemm_mfma_lds<TI, BM, BN, BK, WM, WN, LA, LB, S>), dim3(groups), dim3(WM * WN * 64), 0,
-                           s, g);
+        hipLaunchKernelGGL((gemm_mfma_lds<TI, BM, BN, BK, WM, WN, LA, LB, S, EM>), dim3(groups), dim3(WM * WN * 64),
+                           0, s, g);
     else
-        hipLaunchKernelGGL((gemm_mfma<TI, BM, BN, BK, WM, WN, LA, LB>), dim3(groups), dim3(WM * WN * 64), 0, s, g);
+        hipLaunchKernelGGL((gemm_mfma<TI, BM, BN, BK, WM, WN, LA, LB, EM>), dim3(groups), dim3(WM * WN * 64), 0, s, g);
+}
+
+// The instantiation for the arguments: split-K partials, fused epilogue, or
+// plain stores.
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
+hipError_t launch_mfma(const GemmArgs &g, hipStream_t s) {
+    if (g.splits > 1) launch_mode<TI, BM, BN, BK, WM, WN, LA, LB, S, EM_SPLIT>(g, s);
+    else if (g.epi) launch_mode<TI, BM, BN, BK, WM, WN, LA, LB, S, EM_FUSED>(g, s);
+    else launch_mode<TI, BM, BN, BK, WM, WN, LA, LB, S, EM_STORE>(g, s);
     return hipGetLastError();
 }
 

@@ -67,6 +67,35 @@ SKINNY = {
 }
 
 
+# Shapes for the split-K and batched measurements (few output tiles and a long
+# K; a stack of attention-score-sized products). Not among the five workloads.
+EXTRA = {
+    w.name: w for w in [
+        Workload("splitk_512x512x16384_bf16", 512, 512, 16384, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
+        Workload("splitk_128x4096x8192_bf16", 128, 4096, 8192, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
+        Workload("splitk_256x256x32768_bf16", 256, 256, 32768, "bf16", "f32", ("normal", 0.02), ("normal", 0.02)),
+        Workload("bmm_1024x1024x128_bf16", 1024, 1024, 128, "bf16", "bf16", ("normal", 1.0), ("normal", 1.0)),
+    ]
+}
+
+
+def find(name: str) -> Workload:
+    """A workload by name from any of the tables."""
+    for table in (WORKLOADS, SKINNY, EXTRA):
+        if name in table:
+            return table[name]
+    raise KeyError(f"unknown workload {name!r}")
+
+
+def make_batch(w: Workload, count: int, seed: int = 0):
+    """(A, B) stacks [count, M, K] and [count, K, N] (same recipe, drawn in one go)."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = TORCH_DTYPES[w.in_dtype]
+    a = _draw((count, w.M, w.K), w.a_dist, gen).to(dt)
+    b = _draw((count, w.K, w.N), w.b_dist, gen).to(dt)
+    return a, b
+
+
 def _draw(shape, dist, gen):
     if dist[0] == "uniform":
         return torch.rand(shape, generator=gen, dtype=torch.float32) * 2.0 - 1.0
