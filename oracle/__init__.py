@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for C = A @ B -- TEST INFRASTRUCTURE ONLY.
+"""Plain fp64 CPU oracle for C = A @ B, its fused epilogue and attention -- TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package. It shares no code with the HIP library and never imports
@@ -39,6 +39,9 @@ def _load():
         lib.ref_gemm_rows.argtypes = [i64, i64, i64, i64, ctypes.c_int, p, i64, i64, p, i64, i64, p]
         d, c = ctypes.c_double, ctypes.c_int
         lib.ref_epilogue.argtypes = [i64, i64, p, i64, d, d, c, p, i64, i64, c, p, i64, c, c, p, i64]
+        lib.ref_attention.argtypes = [i64, i64, i64, i64, i64, c, p, i64, i64, i64, p, i64, i64, i64,
+                                      p, i64, i64, i64, d, c, p, p]
+        lib.ref_attention.restype = c
         _lib = lib
     return _lib
 
@@ -170,3 +173,38 @@ def epilogue(p: np.ndarray, alpha=1.0, beta=0.0, r_bits=None, r_dtype=None,
 def gemm_ex(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, **epi) -> np.ndarray:
     """The product followed by the fused epilogue (arguments of `epilogue`)."""
     return epilogue(gemm(a_bits, b_bits, dtype), **epi)
+
+
+def attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dtype: str,
+              scale=None, causal=False):
+    """softmax(scale * Q K^T [causal mask]) V in fp64 (ref_attention in ref_gemm.c).
+
+    q_bits [batch, heads, seq_q, dim], k_bits / v_bits [batch, heads, seq_kv, dim]:
+    views of raw bits with any non-negative strides and a unit stride along
+    dim. scale defaults to 1/sqrt(dim) (taken as given otherwise, in fp64).
+    Returns (O [batch, heads, seq_q, dim] fp64, lse [batch, heads, seq_q] fp64).
+    """
+    if q_bits.ndim != 4 or k_bits.ndim != 4 or v_bits.ndim != 4:
+        raise ValueError("attention takes [batch, heads, seq, dim] arrays")
+    B, H, Sq, D = q_bits.shape
+    if k_bits.shape[:2] != (B, H) or v_bits.shape[:2] != (B, H) or k_bits.shape != v_bits.shape \
+            or k_bits.shape[3] != D:
+        raise ValueError("Q, K, V shapes disagree")
+    Skv = k_bits.shape[2]
+    ptrs, strides = [], []
+    for x in (q_bits, k_bits, v_bits):
+        ptr, st = _operand(x, dtype)
+        if D > 1 and st[3] != 1:
+            raise ValueError("oracle attention needs a unit stride along head_dim")
+        ptrs.append(ptr)
+        strides.append(st[:3])
+    if scale is None:
+        scale = 1.0 / np.sqrt(D) if D > 0 else 1.0
+    o = np.zeros((B, H, Sq, D), dtype=np.float64)
+    lse = np.zeros((B, H, Sq), dtype=np.float64)
+    rc = _load().ref_attention(B, H, Sq, Skv, D, _CODES[dtype], ptrs[0], *strides[0], ptrs[1], *strides[1],
+                               ptrs[2], *strides[2], float(scale), 1 if causal else 0, o.ctypes.data,
+                               lse.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle could not allocate its score row")
+    return o, lse

@@ -1,5 +1,6 @@
 /*
- * Plain fp64 CPU oracle for the dense matrix product C = A @ B.
+ * Plain fp64 CPU oracle for the dense matrix product C = A @ B, its fused
+ * epilogue, and the attention forward pass (softmax(Q K^T) V).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
  * call this file: only the test suite, the smoke check and the benchmark's
@@ -286,4 +287,69 @@ void ref_epilogue(int64_t M, int64_t N, const double *P, int64_t ldp,
             if (bias) v += dec_at(bias_dtype, bias, (per_row ? i : j) * sbias);
             out[i * ldo + j] = ref_act(v, act);
         }
+}
+
+/*
+ * Attention forward, the plain definition, for every (batch b, head h):
+ *
+ *   s[i][j] = scale * sum_d Q[i][d] K[j][d]            for allowed j
+ *   O[i][:] = sum_j exp(s[i][j] - m_i) V[j][:] / l_i,   m_i = max_j s[i][j],
+ *             l_i = sum_j exp(s[i][j] - m_i),           lse_i = m_i + log(l_i)
+ *
+ * ("如何用Triton手写Kernel优化矩阵乘与Flash Attention？", the section on Flash
+ * Attention and online softmax: scores are a block of Q times K transposed
+ * divided by sqrt(head_dim), softmax along the keys, then a weighted sum of
+ * V; the blockwise running-max form computes the same softmax.) Readings:
+ *  - allowed j: all j < seq_kv; with causal != 0 only j <= i (the page's
+ *    causal mask keeps keys whose index does not exceed the query's;
+ *    excluded keys get weight exactly 0);
+ *  - softmax subtracts the row maximum first (the stable form), in fp64;
+ *  - Q, K, V elements at ptr + b*sb + h*sh + row*ss + d (element strides,
+ *    d stride 1), decoded exactly; O and lse are row-major fp64
+ *    [batch][heads][seq_q][head_dim] and [batch][heads][seq_q].
+ */
+int ref_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_kv, int64_t dim, int dtype,
+                  const void *Q, int64_t qb, int64_t qh, int64_t qs,
+                  const void *K, int64_t kb, int64_t kh, int64_t ks,
+                  const void *V, int64_t vb, int64_t vh, int64_t vs,
+                  double scale, int causal, double *O, double *lse) {
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(seq_kv > 0 ? seq_kv : 1));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for collapse(3) schedule(dynamic, 4)
+        for (int64_t b = 0; b < batch; ++b)
+            for (int64_t h = 0; h < heads; ++h)
+                for (int64_t i = 0; i < seq_q; ++i) {
+                    if (!s) continue;
+                    const int64_t qo = b * qb + h * qh + i * qs;
+                    const int64_t n = causal ? (i + 1 < seq_kv ? i + 1 : seq_kv) : seq_kv;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < n; ++j) {
+                        const int64_t ko = b * kb + h * kh + j * ks;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < dim; ++d) dot += dec_at(dtype, Q, qo + d) * dec_at(dtype, K, ko + d);
+                        s[j] = scale * dot;
+                        if (s[j] > m) m = s[j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        s[j] = exp(s[j] - m);
+                        l += s[j];
+                    }
+                    double *o = O + ((b * heads + h) * seq_q + i) * dim;
+                    for (int64_t d = 0; d < dim; ++d) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < n; ++j) acc += s[j] * dec_at(dtype, V, b * vb + h * vh + j * vs + d);
+                        o[d] = n > 0 ? acc / l : 0.0;
+                    }
+                    if (lse) lse[(b * heads + h) * seq_q + i] = n > 0 ? m + log(l) : -INFINITY;
+                }
+        free(s);
+    }
+    return fail ? -1 : 0;
 }

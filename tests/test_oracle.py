@@ -434,3 +434,87 @@ def test_epilogue_brute_force(oracle_mod, dtype):
                     v = Fraction(0)
                 scale = abs(fa * p[i][j]) + abs(fb * rv) + 1
                 assert abs(Fraction(float(got[i, j])) - v) <= scale * Fraction(1, 2 ** 50), (trial, i, j)
+
+
+# ---- attention ------------------------------------------------------------------
+
+def attn_bits(shape, dtype, seed, scale=1.0):
+    t = (torch.randn(shape, generator=torch.Generator().manual_seed(seed)) * scale).to(inputs.TORCH_DTYPES[dtype])
+    return t, inputs.bits(t, dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_zero_queries_average_the_values(oracle_mod, causal):
+    """Q = 0: every score is 0, so O is the plain mean of the allowed V rows and lse = log(count)."""
+    B, H, Sq, Skv, D = 2, 3, 6, 6, 8
+    q = np.zeros((B, H, Sq, D), dtype=np.uint16)  # +0 in bf16
+    _, kb = attn_bits((B, H, Skv, D), "bf16", 1)
+    vt, vb = attn_bits((B, H, Skv, D), "bf16", 2)
+    o, lse = oracle_mod.attention(q, kb, vb, "bf16", causal=causal)
+    v = vt.double().numpy()
+    for i in range(Sq):
+        n = i + 1 if causal else Skv
+        assert np.allclose(o[:, :, i], v[:, :, :n].mean(axis=2), rtol=0, atol=1e-15)
+        assert np.allclose(lse[:, :, i], math.log(n), rtol=0, atol=1e-15)
+
+
+def test_attention_causal_first_row_and_single_key(oracle_mod):
+    _, qb = attn_bits((1, 2, 5, 16), "f16", 3)
+    _, kb = attn_bits((1, 2, 5, 16), "f16", 4)
+    vt, vb = attn_bits((1, 2, 5, 16), "f16", 5)
+    o, lse = oracle_mod.attention(qb, kb, vb, "f16", causal=True)
+    assert np.array_equal(o[:, :, 0], vt[:, :, 0].double().numpy())  # one allowed key: weight exactly 1
+    # lse of that row is the single score itself
+    q0 = oracle_mod.decode(qb[:, :, 0], "f16")
+    k0 = oracle_mod.decode(kb[:, :, 0], "f16")
+    assert np.allclose(lse[:, :, 0], (q0 * k0).sum(-1) / 4.0, rtol=1e-15, atol=1e-15)
+    # seq_kv = 1, no mask: every row is V[0]
+    o1, _ = oracle_mod.attention(qb, kb[:, :, :1], vb[:, :, :1], "f16")
+    assert np.array_equal(o1, np.broadcast_to(vt[:, :, :1].double().numpy(), o1.shape))
+
+
+def test_attention_invariances(oracle_mod):
+    B, H, Sq, Skv, D = 1, 2, 7, 9, 16
+    _, qb = attn_bits((B, H, Sq, D), "bf16", 6)
+    kt, _ = attn_bits((B, H, Skv, D), "bf16", 7)
+    # column 3 of K holds small integers, so the shift below is exact in bf16
+    kt[..., 3] = torch.randint(-4, 5, (B, H, Skv), generator=torch.Generator().manual_seed(12)).to(torch.bfloat16)
+    kb = inputs.bits(kt, "bf16")
+    vt, vb = attn_bits((B, H, Skv, D), "bf16", 8)
+    o, lse = oracle_mod.attention(qb, kb, vb, "bf16")
+    # permuting keys together with their values changes nothing (no mask)
+    perm = np.random.default_rng(0).permutation(Skv)
+    op, lp = oracle_mod.attention(qb, np.ascontiguousarray(kb[:, :, perm]), np.ascontiguousarray(vb[:, :, perm]), "bf16")
+    assert np.allclose(op, o, rtol=0, atol=1e-13) and np.allclose(lp, lse, rtol=0, atol=1e-13)
+    # adding the same vector u to every key shifts each row's scores by scale*q.u: O unchanged, lse shifted
+    u = torch.zeros(D)
+    u[3] = 2.0
+    k2 = (kt.float() + u).to(torch.bfloat16)
+    assert torch.equal(k2.float() - kt.float(), u.expand_as(kt))  # the shift is exact in bf16 here
+    o2, l2 = oracle_mod.attention(qb, inputs.bits(k2, "bf16"), vb, "bf16")
+    qd = oracle_mod.decode(qb, "bf16")
+    assert np.allclose(o2, o, rtol=0, atol=1e-13)
+    assert np.allclose(l2 - lse, qd[..., 3] * 2.0 / 4.0, rtol=0, atol=1e-13)
+    # linear in V: small integers keep V1 + V2 exact in bf16
+    g = torch.Generator().manual_seed(9)
+    v1 = torch.randint(-4, 5, (B, H, Skv, D), generator=g).to(torch.bfloat16)
+    v2 = torch.randint(-4, 5, (B, H, Skv, D), generator=g).to(torch.bfloat16)
+    o1, _ = oracle_mod.attention(qb, kb, inputs.bits(v1, "bf16"), "bf16")
+    o2_, _ = oracle_mod.attention(qb, kb, inputs.bits(v2, "bf16"), "bf16")
+    o12, _ = oracle_mod.attention(qb, kb, inputs.bits(v1 + v2, "bf16"), "bf16")
+    assert np.allclose(o12, o1 + o2_, rtol=0, atol=1e-13)
+
+
+def test_attention_one_hot_limit_and_large_scores(oracle_mod):
+    """A key aligned with the query and scores in the thousands: weight ~1 on it, no overflow."""
+    D = 16
+    q = torch.zeros(1, 1, 3, D)
+    q[0, 0, :, 0] = 64.0
+    k = torch.randn(1, 1, 5, D, generator=torch.Generator().manual_seed(10)) * 0.1
+    k[0, 0, 2, 0] = 64.0   # score 64*64/4 = 1024 for key 2, the others near 0
+    v = torch.randn(1, 1, 5, D, generator=torch.Generator().manual_seed(11))
+    qb, kb, vb = (inputs.bits(t.to(torch.float16), "f16") for t in (q, k, v))
+    o, lse = oracle_mod.attention(qb, kb, vb, "f16")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.allclose(o[0, 0], np.broadcast_to(oracle_mod.decode(vb[0, 0, 2], "f16"), (3, D)), rtol=0, atol=1e-300)
+    assert np.allclose(lse[0, 0], 1024.0, rtol=1e-15, atol=0)  # the other keys add exp(-1024) ~ 0
