@@ -118,6 +118,49 @@ def cpu_baseline(w, a_cpu, b_cpu, target_s=10.0):
                       f"{dt:.2f} s wall, fp64 k-ascending sums"}
 
 
+def bench_attention(args):
+    """Attention forward: O = softmax(QK^T/sqrt(d) [causal]) V, [batch, heads, seq, head_dim] bf16."""
+    import torch
+
+    import dense_gemm_07_amd as dg
+
+    B, H, S, D = max(1, args.batch), args.heads, args.seq, args.head_dim
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator().manual_seed(0)
+    q, k, v = (torch.randn((B, H, S, D), generator=gen).to(torch.bfloat16).to(dev) for _ in range(3))
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    step = lambda: dg.attention(q, k, v, out=o, causal=args.causal, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # Useful work: two S x S x D products per (batch, head); a causal mask keeps
+    # the S (S + 1) / 2 allowed (query, key) pairs.
+    pairs = S * (S + 1) / 2 if args.causal else S * S
+    flops = 4.0 * B * H * pairs * D
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    result = {
+        "metric": "attention forward TFLOP/s (bf16, seq 8192, head_dim 64) on 1 MI355X",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"attention fwd b{B} h{H} s{S} d{D}{' causal' if args.causal else ''} bf16",
+                   "batch": B, "heads": H, "seq": S, "head_dim": D, "causal": args.causal},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +183,12 @@ def main():
     ap.add_argument("--batch", type=int, default=1, help="time a strided batch of this many products (dg_gemm_ex)")
     ap.add_argument("--split-k", action="store_true",
                     help="time dg_gemm_ex with a workspace (the library may split K)")
+    ap.add_argument("--attention", action="store_true",
+                    help="time the attention forward kernel instead (--batch, --heads, --seq, --head-dim, --causal)")
+    ap.add_argument("--heads", type=int, default=16)
+    ap.add_argument("--seq", type=int, default=8192)
+    ap.add_argument("--head-dim", type=int, default=64)
+    ap.add_argument("--causal", action="store_true")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(args.workload, *args.record_traffic, args.copy_mib, args.commands)
@@ -166,6 +215,9 @@ def main():
         return
     if not os.path.exists(LIB):
         build()
+    if args.attention:
+        bench_attention(args)
+        return
     w = inputs.find(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -10,6 +10,7 @@ fallback: if the library is missing, every call raises.
     C = gemm_ex(A, B, bias=b, activation="relu")       # fused epilogue
     C = gemm_ex(A3, B3)                 # strided batch: [batch, M, K] @ [batch, K, N]
     Y = linear(X, W, b)                 # autograd: Y = X @ W^T + b
+    O, lse = attention(Q, K, V, causal=True)           # softmax(QK^T/sqrt(d)) V, blockwise
 """
 import ctypes
 import os
@@ -19,6 +20,7 @@ from .build import LIB
 __all__ = [
     "Config", "DGError", "gemm", "gemm_config", "autotune", "select_config", "candidates",
     "Epilogue", "Batch", "gemm_ex", "autotune_ex", "workspace_size", "select_config_ex", "matmul", "linear",
+    "attention",
     "validate", "tile_coords", "grid_shape", "cache_clear", "cache_save", "cache_load",
     "cache_size", "library", "DG_F32", "DG_F16", "DG_BF16", "VARIANT_SIMT", "VARIANT_MFMA",
 ]
@@ -88,6 +90,9 @@ def library():
         lib.dg_autotune_ex.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch), _p, _i64,
                                                   _i32, ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_float)]
         lib.dg_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(Config), ctypes.POINTER(_i64)]
+        _st = ctypes.POINTER(_i64)
+        lib.dg_attention_fwd.argtypes = [_i64] * 5 + [_p, _st, _p, _st, _p, _st, _p, _st, _p, ctypes.c_int,
+                                                      ctypes.c_int, ctypes.c_float, _i32, _p]
         lib.dg_num_candidates.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.dg_num_candidates.restype = _i32
         lib.dg_get_candidate.argtypes = [_i32, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Config)]
@@ -100,7 +105,7 @@ def library():
         lib.dg_last_error.restype = ctypes.c_char_p
         for name in ("dg_gemm", "dg_gemm_config", "dg_autotune", "dg_select_config", "dg_select_config_ex",
                      "dg_validate",
-                     "dg_gemm_ex", "dg_autotune_ex", "dg_workspace_size",
+                     "dg_gemm_ex", "dg_autotune_ex", "dg_workspace_size", "dg_attention_fwd",
                      "dg_get_candidate", "dg_tile_coords", "dg_grid_shape", "dg_cache_clear",
                      "dg_cache_save", "dg_cache_load"):
             getattr(lib, name).restype = ctypes.c_int
@@ -459,3 +464,43 @@ def linear(x, weight, bias=None):
     global _fns
     _fns = _fns or _autograd_fn()
     return _fns[1].apply(x, weight, bias)
+
+
+# ---- attention forward ------------------------------------------------------------
+
+def attention(q, k, v, out=None, out_dtype=None, scale=None, causal=False, return_lse=False, stream=None):
+    """O = softmax(scale * Q K^T [causal]) V on the HIP kernel (dg_attention_fwd).
+
+    q: [batch, heads, seq_q, head_dim]; k, v: [batch, heads, seq_kv, head_dim]
+    (any strides with a unit head_dim stride). scale defaults to
+    1/sqrt(head_dim). Returns O (and the fp32 log-sum-exp [batch, heads,
+    seq_q] when return_lse).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("attention takes [batch, heads, seq, head_dim] tensors")
+    B, H, Sq, D = q.shape
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != D:
+        raise ValueError(f"shapes disagree: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+        if D > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name} needs a unit stride along head_dim")
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if tuple(out.shape) != (B, H, Sq, D) or (D > 1 and out.stride(3) != 1):
+        raise ValueError("out must be [batch, heads, seq_q, head_dim] with a unit head_dim stride")
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+
+    def strides(t):
+        return (_i64 * 3)(*t.stride()[:3])
+
+    _check(library().dg_attention_fwd(B, H, Sq, k.shape[2], D, q.data_ptr(), strides(q), k.data_ptr(),
+                                      strides(k), v.data_ptr(), strides(v), out.data_ptr(), strides(out),
+                                      lse.data_ptr() if lse is not None else None, _dtype_code(q.dtype),
+                                      _dtype_code(out.dtype), float(scale) if scale else 0.0,
+                                      1 if causal else 0, _stream(q, stream)))
+    return (out, lse) if return_lse else out

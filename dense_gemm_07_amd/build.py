@@ -16,7 +16,7 @@ LIB = os.path.join(LIBDIR, "libdg.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dg_host.cpp", "simt.hip", "split_reduce.hip"] + [
+SOURCES = ["dg_host.cpp", "simt.hip", "split_reduce.hip", "attention.hip"] + [
     f"mfma_{t}_{m}.hip" for t in ("bf16", "f16") for m in ("kc_rc", "kc_kc", "rc_rc", "rc_kc", "gn", "unaligned")]
 
 COMMON = [
@@ -43,12 +43,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
+def build(verbose: bool = False, jobs: int = 0, only=None) -> str:
+    """Compile every unit (or, with `only`, just those units, reusing the other
+    objects from an earlier build) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)), 16)
+    todo = SOURCES if not only else [s for s in SOURCES if s in only]
+    if only and len(todo) != len(set(only)):
+        raise ValueError(f"unknown sources in {only}")
+    jobs = jobs or min(len(todo), max(1, (os.cpu_count() or 4)), 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        list(ex.map(lambda s: _compile(s, verbose), todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"objects missing (run a full build): {missing}")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
@@ -59,4 +68,5 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    only = next((a.split("=", 1)[1].split(",") for a in sys.argv if a.startswith("--only=")), None)
+    print(build(verbose="-v" in sys.argv, only=only))

@@ -1,0 +1,32 @@
+// Internal declarations of the attention forward kernel. Not part of the C-ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Q, K, V, O are [batch][heads][seq][head_dim] with element strides
+// (batch, head, seq) and a unit stride along head_dim; lse (may be NULL) is
+// fp32 [batch][heads][seq_q], contiguous.
+struct AttnArgs {
+    const void *Q, *K, *V;
+    void *O;
+    float *lse;
+    int32_t batch, heads, seq_q, seq_kv;
+    int64_t qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os;
+    float scale_log2;   // softmax scale times log2(e): the kernel exponentiates with exp2
+    int32_t out_dtype;  // dg_dtype of O
+    int32_t q_blocks;   // query blocks per (batch, head)
+    int32_t causal;
+};
+
+constexpr int kAttnBlockQ = 128;  // queries per workgroup (4 waves x 32)
+constexpr int kAttnBlockKV = 64;  // keys per step
+constexpr int kAttnStages = 3;    // K/V blocks in the LDS ring
+
+// Launches the kernel for an input dtype / head_dim pair; hipErrorInvalidValue
+// if none is compiled.
+hipError_t launch_attention(const AttnArgs &a, int in_dtype, int head_dim, hipStream_t s);
+
+}  // namespace dg

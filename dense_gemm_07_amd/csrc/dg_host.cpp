@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cinttypes>
 #include <cstdarg>
 #include <cstdio>
@@ -15,6 +16,7 @@
 #include <tuple>
 #include <vector>
 
+#include "attention.hpp"
 #include "dg.h"
 #include "dg_internal.hpp"
 
@@ -729,6 +731,71 @@ dg_status dg_gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam
     const dg_config c = cfg ? *cfg : choose(p, workspace_bytes);
     if (!cfg) log_choice("gemm_ex", p, c);
     return launch(p, c, (hipStream_t)stream, workspace, workspace_bytes);
+}
+
+dg_status dg_attention_fwd(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_kv, int64_t head_dim,
+                           const void *Q, const int64_t *q_strides, const void *K, const int64_t *k_strides,
+                           const void *V, const int64_t *v_strides, void *O, const int64_t *o_strides, float *lse,
+                           dg_dtype in_dtype, dg_dtype out_dtype, float scale, int32_t causal, void *stream) {
+    g_last_error.clear();
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(DG_ERR_INVALID_VALUE, "unknown dtype");
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_kv < 0 || head_dim < 0)
+        return fail(DG_ERR_INVALID_VALUE, "negative size");
+    const int64_t lim = (int64_t)1 << 30;
+    if (seq_q >= lim || seq_kv >= lim || batch * heads >= lim)
+        return fail(DG_ERR_UNSUPPORTED, "sizes too large for the attention kernel");
+    if (batch == 0 || heads == 0 || seq_q == 0) return DG_OK;
+    if (!q_strides || !k_strides || !v_strides || !o_strides) return fail(DG_ERR_INVALID_VALUE, "strides are NULL");
+    if (!Q || !O || (seq_kv > 0 && (!K || !V))) return fail(DG_ERR_INVALID_VALUE, "a tensor pointer is NULL");
+    for (const int64_t *st : {q_strides, k_strides, v_strides, o_strides})
+        for (int i = 0; i < 3; ++i)
+            if (st[i] < 0) return fail(DG_ERR_INVALID_VALUE, "negative stride");
+    if (in_dtype == DG_F32) return fail(DG_ERR_UNSUPPORTED, "attention takes fp16 or bf16 Q, K, V");
+    if (head_dim != 64) return fail(DG_ERR_UNSUPPORTED, "head_dim %" PRId64 " (supported: 64)", head_dim);
+    // O's rows must not overlap: (batch, head, seq, dim) strides nested when sorted.
+    if (!nested({{batch, o_strides[0]}, {heads, o_strides[1]}, {seq_q, o_strides[2]}, {head_dim, 1}}))
+        return fail(DG_ERR_INVALID_VALUE, "O strides make its elements overlap");
+    const struct {
+        const void *p;
+        const int64_t *st;
+        const char *name;
+    } ins[] = {{Q, q_strides, "Q"}, {K, k_strides, "K"}, {V, v_strides, "V"}};
+    for (const auto &t : ins) {
+        if (seq_kv == 0 && t.p != Q) continue;  // K and V are not read
+        if (!aligned16(t.p) || t.st[0] % 8 || t.st[1] % 8 || t.st[2] % 8)
+            return fail(DG_ERR_UNSUPPORTED, "%s needs a 16-byte aligned base and strides that are multiples of 8",
+                        t.name);
+    }
+    if ((uintptr_t)O % (uintptr_t)elem_size(out_dtype)) return fail(DG_ERR_INVALID_VALUE, "O misaligned");
+    // The key-block loads address one (batch, head) with 31-bit byte offsets,
+    // including the blocks queued past the end.
+    const i128 span = (i128)(seq_kv + kAttnStages * kAttnBlockKV) * std::max(k_strides[2], v_strides[2]) * 2;
+    if (span >= ((i128)1 << 31)) return fail(DG_ERR_UNSUPPORTED, "K/V of one head span more than 2 GiB");
+    const int64_t q_blocks = (seq_q + kAttnBlockQ - 1) / kAttnBlockQ;
+    if (batch * heads * q_blocks >= ((int64_t)1 << 31) / 256)
+        return fail(DG_ERR_UNSUPPORTED, "too many query blocks");
+    AttnArgs a{};
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.lse = lse;
+    a.batch = (int32_t)batch;
+    a.heads = (int32_t)heads;
+    a.seq_q = (int32_t)seq_q;
+    a.seq_kv = (int32_t)seq_kv;
+    a.qb = q_strides[0], a.qh = q_strides[1], a.qs = q_strides[2];
+    a.kb = k_strides[0], a.kh = k_strides[1], a.ks = k_strides[2];
+    a.vb = v_strides[0], a.vh = v_strides[1], a.vs = v_strides[2];
+    a.ob = o_strides[0], a.oh = o_strides[1], a.os = o_strides[2];
+    const float sc = (scale > 0.0f) ? scale : 1.0f / std::sqrt((float)head_dim);
+    a.scale_log2 = sc * 1.44269504088896340736f;
+    a.out_dtype = out_dtype;
+    a.q_blocks = (int32_t)q_blocks;
+    a.causal = causal ? 1 : 0;
+    const hipError_t err = launch_attention(a, in_dtype, (int)head_dim, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(DG_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
+    return DG_OK;
 }
 
 dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count, const dg_config *cfg,

@@ -265,6 +265,40 @@ dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count
                             int64_t *bytes);
 
 /*
+ * Attention forward: for every batch b and head h,
+ *
+ *   O[i][:] = sum_j softmax_j(scale * Q[i]·K[j]) V[j][:],   lse[i] = log sum_j exp(scale * Q[i]·K[j])
+ *
+ * over the allowed keys j (all j < seq_kv; with causal != 0 only j <= i).
+ * This is the blockwise, online-softmax attention of "如何用Triton手写Kernel优化
+ * 矩阵乘与Flash Attention？" (its Flash Attention section): one program per
+ * query block walks the key blocks keeping a running maximum and sum, so
+ * the score matrix is never stored.
+ *  Q: [batch][heads][seq_q][head_dim]; K, V: [batch][heads][seq_kv][head_dim];
+ *     O: [batch][heads][seq_q][head_dim]. DEVICE pointers; each *_strides is
+ *     a host array of 3 element strides (batch, head, seq); the head_dim
+ *     stride is 1. Q, K, V (in_dtype, fp16 or bf16) need 16-byte aligned
+ *     bases and batch/head/seq strides that are multiples of 8 elements.
+ *  lse: NULL, or a DEVICE fp32 array [batch][heads][seq_q] (contiguous) that
+ *     receives the natural-log sum of exponentials per query (-inf for a query
+ *     with no allowed key).
+ *  out_dtype: O's dtype (f32, f16 or bf16), rounded from the fp32 result.
+ *  scale: the score scale; <= 0 (or NaN) selects 1 / sqrt(head_dim).
+ *  Numerics: fp32 scores, softmax and accumulation; the softmax weights are
+ *     rounded to in_dtype for the product with V (the matrix cores take 16-bit
+ *     operands); the normalising sum uses the unrounded weights.
+ *  Supported: head_dim 64. Other head_dim values, in_dtype f32, or layouts
+ *     outside the above return DG_ERR_UNSUPPORTED; bad arguments return
+ *     DG_ERR_INVALID_VALUE. Any size may be 0 (nothing to do; seq_kv == 0
+ *     writes O = 0 and lse = -inf). seq_q, seq_kv < 2^30.
+ */
+dg_status dg_attention_fwd(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_kv, int64_t head_dim,
+                           const void *Q, const int64_t *q_strides, const void *K, const int64_t *k_strides,
+                           const void *V, const int64_t *v_strides, void *O, const int64_t *o_strides,
+                           float *lse, dg_dtype in_dtype, dg_dtype out_dtype, float scale, int32_t causal,
+                           void *stream);
+
+/*
  * The config dg_gemm would use, without any GPU work. The pointers are only
  * inspected for alignment (they may be NULL: then taken as 16-byte aligned).
  * *from_cache (may be NULL) is set to 1 if the config came from the cache.

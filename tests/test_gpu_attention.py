@@ -1,0 +1,183 @@
+"""GPU parity of the attention forward kernel against the CPU oracle (fp64).
+
+Every call goes through the C-ABI (dg_attention_fwd via the binding). Bar,
+derived from the arithmetic: the softmax weights are rounded once to the
+input type (unit roundoff u = 2^-9 bf16, 2^-12 fp16) for the product with V,
+so each output moves by at most u * max|V| of its row's keys; fp32 scores,
+exponentials and sums add about 1e-5 relative; then half an ulp of O's
+dtype. Tolerance: 2u * max|V| + 1e-5 * (1 + max|V|) + 1/2 ulp_out(|O|).
+lse (fp32, from fp32 scores): 1e-4 * (1 + |lse|).
+Closed forms are checked tighter: Q = 0 gives the mean of the allowed V
+rows (every weight is exactly 1), and the first row of a causal mask is V[0].
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_07_amd as dg
+import oracle
+from dense_gemm_07_amd import inputs
+from helpers import ulp
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TD = inputs.TORCH_DTYPES
+U_IN = {"bf16": 2.0 ** -9, "f16": 2.0 ** -12}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build()
+    dg.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def draw(shape, dtype, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * std).to(TD[dtype])
+
+
+def layout(t, kind):
+    """Device copy of a [B, H, S, D] CPU tensor stored as BHSD or BSHD (heads interleaved)."""
+    if kind == "bhsd":
+        return t.to(DEV)
+    return t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+
+
+def check(q, k, v, dtype, out_dtype, causal, kinds=("bhsd", "bhsd", "bhsd"), scale=None, what=""):
+    note(what)
+    qd, kd, vd = (layout(t, kind) for t, kind in zip((q, k, v), kinds))
+    o, lse = dg.attention(qd, kd, vd, out_dtype=TD[out_dtype], scale=scale, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention(inputs.bits(q, dtype), inputs.bits(k, dtype), inputs.bits(v, dtype), dtype,
+                                    scale=scale, causal=causal)
+    got = o.double().cpu().numpy()
+    vmax = np.abs(v.double().numpy()).max(axis=2, keepdims=True)  # per (batch, head), over keys
+    tol = 2 * U_IN[dtype] * vmax + 1e-5 * (1 + vmax) + 0.5 * ulp(out_dtype, np.maximum(np.abs(got), np.abs(ref)))
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance, max err {err.max():.3e}, "
+                           f"first {np.argwhere(bad)[:3].tolist()}")
+    gl = lse.double().cpu().numpy()
+    finite = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(gl), finite), f"{what}: lse finiteness differs"
+    assert np.all(np.abs(gl[finite] - ref_lse[finite]) <= 1e-4 * (1 + np.abs(ref_lse[finite]))), f"{what}: lse"
+    return float(err.max())
+
+
+SHAPES = [  # (batch, heads, seq_q, seq_kv)
+    (1, 1, 1, 1),
+    (1, 1, 128, 64),
+    (2, 3, 100, 77),      # ragged both ways
+    (1, 2, 300, 513),
+    (2, 2, 257, 1000),
+    (1, 1, 64, 4096),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype,out_dtype", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+def test_attention_random(shape, causal, dtype, out_dtype):
+    B, H, Sq, Skv = shape
+    q, k, v = (draw((B, H, s, 64), dtype, seed) for s, seed in ((Sq, 1), (Skv, 2), (Skv, 3)))
+    check(q, k, v, dtype, out_dtype, causal, what=f"{shape} causal={causal} {dtype}->{out_dtype}")
+
+
+@pytest.mark.parametrize("kinds", [("bshd", "bshd", "bshd"), ("bhsd", "bshd", "bhsd")])
+def test_attention_interleaved_heads(kinds):
+    q, k, v = (draw((2, 4, s, 64), "bf16", seed) for s, seed in ((190, 4), (333, 5), (333, 6)))
+    check(q, k, v, "bf16", "bf16", False, kinds=kinds, what=f"layouts {kinds}")
+    check(q[:, :, :190], k[:, :, :190], v[:, :, :190], "bf16", "bf16", True, kinds=kinds, what=f"causal {kinds}")
+
+
+def test_attention_large_scores_and_custom_scale():
+    """Scores in the hundreds (no overflow thanks to the running max) and an explicit scale."""
+    q = draw((1, 2, 200, 64), "f16", 7, std=4.0)
+    k = draw((1, 2, 300, 64), "f16", 8, std=4.0)
+    v = draw((1, 2, 300, 64), "f16", 9)
+    check(q, k, v, "f16", "f32", False, what="large scores")
+    check(q, k, v, "f16", "f32", True, scale=0.05, what="scale 0.05")
+
+
+def test_attention_zero_queries_average_values():
+    B, H, S, D = 1, 2, 150, 64
+    q = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
+    k = draw((B, H, S, D), "bf16", 10)
+    v = draw((B, H, S, D), "bf16", 11)
+    for causal in (False, True):
+        note(f"zero queries causal={causal}")
+        o, lse = dg.attention(q.to(DEV), k.to(DEV), v.to(DEV), out_dtype=torch.float32, causal=causal,
+                              return_lse=True)
+        torch.cuda.synchronize()
+        vv = v.double().numpy()
+        for i in (0, 1, 63, 64, 127, 128, 149):
+            n = i + 1 if causal else S
+            assert np.allclose(o[:, :, i].double().cpu().numpy(), vv[:, :, :n].mean(axis=2), rtol=0, atol=3e-6)
+            assert np.allclose(lse[:, :, i].double().cpu().numpy(), math.log(n), rtol=1e-6, atol=0)
+
+
+def test_attention_causal_first_row_is_v0_and_empty_keys():
+    q, k, v = (draw((2, 2, 70, 64), "f16", s) for s in (12, 13, 14))
+    o = dg.attention(q.to(DEV), k.to(DEV), v.to(DEV), out_dtype=torch.float32, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0].float())
+    # no keys at all: O = 0, lse = -inf
+    o0, l0 = dg.attention(q.to(DEV), k[:, :, :0].to(DEV), v[:, :, :0].to(DEV), return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o0).item() == 0 and torch.isinf(l0).all() and (l0 < 0).all()
+
+
+def test_attention_full_size_sampled():
+    """The measured shape (seq 8192, head_dim 64), causal and not; sampled query rows vs the oracle."""
+    B, H, S, D = 1, 4, 8192, 64
+    q, k, v = (draw((B, H, S, D), "bf16", s) for s in (15, 16, 17))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    rows = np.array([0, 1, 63, 127, 128, 2047, 4096, 8190, 8191])
+    for causal in (False, True):
+        note(f"full size causal={causal}")
+        o, lse = dg.attention(qd, kd, vd, causal=causal, return_lse=True)
+        torch.cuda.synchronize()
+        if not causal:
+            ref, ref_lse = oracle.attention(inputs.bits(q[:, :, rows], "bf16"), inputs.bits(k, "bf16"),
+                                            inputs.bits(v, "bf16"), "bf16")
+        else:  # sampled row i sees keys 0..i: the unmasked oracle on that prefix
+            ref = np.zeros((B, H, len(rows), D))
+            ref_lse = np.zeros((B, H, len(rows)))
+            for t, i in enumerate(rows):
+                r, rl = oracle.attention(inputs.bits(q[:, :, i:i + 1], "bf16"), inputs.bits(k[:, :, :i + 1], "bf16"),
+                                         inputs.bits(v[:, :, :i + 1], "bf16"), "bf16")
+                ref[:, :, t], ref_lse[:, :, t] = r[:, :, 0], rl[:, :, 0]
+        got = o[:, :, rows].double().cpu().numpy()
+        vmax = np.abs(v.double().numpy()).max(axis=2, keepdims=True)
+        tol = 2 * U_IN["bf16"] * vmax + 1e-5 * (1 + vmax) + 0.5 * ulp("bf16", np.maximum(np.abs(got), np.abs(ref)))
+        assert np.all(np.abs(got - ref) <= tol), f"causal={causal} max err {np.abs(got - ref).max()}"
+        gl = lse[:, :, rows].double().cpu().numpy()
+        assert np.all(np.abs(gl - ref_lse) <= 1e-4 * (1 + np.abs(ref_lse)))
+
+
+def test_attention_rejects_unsupported():
+    q = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(dg.DGError) as e:
+        dg.attention(q, q, q)
+    assert e.value.status == 2  # head_dim 32 not compiled
+    q64 = torch.zeros(1, 1, 8, 64, dtype=torch.float32, device=DEV)
+    with pytest.raises(dg.DGError):
+        dg.attention(q64, q64, q64)  # fp32 inputs
+    buf = torch.zeros(1 + 8 * 64, dtype=torch.bfloat16, device=DEV)
+    mis = buf[1:].view(1, 1, 8, 64)
+    with pytest.raises(dg.DGError):
+        dg.attention(mis, mis, mis)  # not 16-byte aligned

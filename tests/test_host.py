@@ -326,3 +326,25 @@ def test_gemm_ex_default_split_choice():
     c, _ = dg.select_config_ex(256, 256, 32768, (32768, 1), (256, 1), (256, 1), BF16, BF16, batch=64,
                                workspace_bytes=1 << 30)
     assert c.k_splits == 1
+
+
+# ---- dg_attention_fwd: argument checks (no GPU work) -------------------------------
+
+def attn_status(B=1, H=1, Sq=8, Skv=8, D=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE, st=(512, 512, 64), dt=BF16, out=BF16):
+    lib = dg.library()
+    arr = lambda t: (ctypes.c_int64 * 3)(*t)
+    return lib.dg_attention_fwd(B, H, Sq, Skv, D, q, arr(st), k, arr(st), v, arr(st), o, arr(st), None, dt, out,
+                                ctypes.c_float(0.0), 0, None)
+
+
+def test_attention_argument_checks():
+    UNSUPPORTED = 2
+    assert attn_status(B=-1) == INVALID
+    assert attn_status(q=None) == INVALID
+    assert attn_status(D=128) == UNSUPPORTED and b"head_dim" in dg.library().dg_last_error()
+    assert attn_status(dt=F32) == UNSUPPORTED
+    assert attn_status(q=FAKE + 2) == UNSUPPORTED           # Q not 16-byte aligned
+    assert attn_status(st=(512, 512, 66)) == UNSUPPORTED    # seq stride not a multiple of 8
+    assert attn_status(st=(512, 512, 32)) == INVALID        # O rows overlap (seq stride < head_dim)
+    assert attn_status(Sq=0) == OK and attn_status(B=0) == OK  # nothing to do
+    assert attn_status(Skv=1 << 30) == UNSUPPORTED
