@@ -28,9 +28,16 @@ COMMON = [
 ]
 
 
+# Per-unit flags. The attention kernel's accumulators stay in ordinary VGPRs
+# (gfx950 MFMA reads and writes them directly): in accumulation registers every
+# softmax step would copy its scores and rescale its output through
+# v_accvgpr_read / v_accvgpr_write.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

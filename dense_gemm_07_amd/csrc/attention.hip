@@ -9,10 +9,12 @@
 //
 // Mapping onto v_mfma_f32_32x32x16 (lane l, register r of a 32x32 result hold
 // row 8*(r/4) + 4*(l/32) + r%4, column l%32):
-//  - Each wave owns 32 queries. It computes S^T = K Q^T, so the 32 queries
-//    are the result's columns: lane l always holds scores of query l%32. The
-//    running max needs one exchange with lane l^32 per key block; the running
-//    sum and the rescaling of O stay per lane.
+//  - Each wave owns kAttnQueryGroups groups of 32 queries. It computes
+//    S^T = K Q^T, so a group's 32 queries are the result's columns: lane l
+//    always holds scores of query l%32 of each group. The running max needs
+//    one exchange with lane l^32 per key block; the running sum and the
+//    rescaling of O stay per lane. Each K or V fragment read from LDS feeds
+//    every group's MFMA.
 //  - O^T += V^T P^T. The MFMA's k index only has to agree between its two
 //    operands. K rows are loaded into LDS with bits 2 and 3 of the row
 //    index swapped, which makes register r of S^T hold key 16*(r/8) +
@@ -27,6 +29,8 @@
 // scores scaled by scale * log2(e); P is rounded to the input type for the
 // second product (the matrix cores take 16-bit operands), the running sum
 // adds the unrounded fp32 weights.
+#include <type_traits>
+
 #include "attention.hpp"
 #include "dg_kernels.hpp"
 
@@ -38,8 +42,9 @@ __device__ __forceinline__ int attn_key_of_row(int i) { return (i & ~12) | ((i &
 template <typename TI, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     constexpr int NW = 4;
+    constexpr int QG = kAttnQueryGroups;  // 32-query groups per wave
     constexpr int BQ = kAttnBlockQ, BKV = kAttnBlockKV, S = kAttnStages;
-    static_assert(BQ == NW * 32, "one 32-query column block per wave");
+    static_assert(BQ == NW * 32 * QG, "QG 32-query column blocks per wave");
     using KT = KTile<BKV, D>;  // K block: rows = keys (permuted), k = head_dim
     using VT = RTile<D, BKV>;  // V block: k = keys, rows = head_dim
     constexpr int K_BYTES = BKV * D * 2, STAGE = 2 * BKV * D * 2;
@@ -60,19 +65,24 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
     const int q0 = qblk * BQ;
-    const int wq0 = q0 + wave * 32;      // this wave's first query
-    const int my_q = wq0 + (lane & 31);  // this lane's query
+    const int wq0 = q0 + wave * 32 * QG;  // this wave's first query; group g holds wq0 + 32g + (l % 32)
+    int my_q[QG];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) my_q[g] = wq0 + 32 * g + (lane & 31);
 
     const uint16_t *Qp = static_cast<const uint16_t *>(a.Q) + (int64_t)b * a.qb + (int64_t)h * a.qh;
     const uint16_t *Kp = static_cast<const uint16_t *>(a.K) + (int64_t)b * a.kb + (int64_t)h * a.kh;
     const uint16_t *Vp = static_cast<const uint16_t *>(a.V) + (int64_t)b * a.vb + (int64_t)h * a.vh;
 
-    // Q^T as the B operand of S^T = K Q^T: lane l holds Q[my_q][16kk + 8*(l/32) + e].
-    u32x4 qf[DK];
+    // Q^T as the B operand of S^T = K Q^T: lane l holds Q[query][16kk + 8*(l/32) + e].
+    u32x4 qf[QG][DK];
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-        qf[kk] = my_q < a.seq_q ? *reinterpret_cast<const u32x4 *>(Qp + (int64_t)my_q * a.qs + 16 * kk + 8 * half)
-                                : u32x4{0u, 0u, 0u, 0u};
+    for (int g = 0; g < QG; ++g)
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk)
+            qf[g][kk] = my_q[g] < a.seq_q
+                            ? *reinterpret_cast<const u32x4 *>(Qp + (int64_t)my_q[g] * a.qs + 16 * kk + 8 * half)
+                            : u32x4{0u, 0u, 0u, 0u};
 
     // Buffer-load descriptors and this lane's share of each block's loads.
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kp, 0, kNumRecords, kRsrcWord3);
@@ -111,68 +121,109 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     int nkv = (a.seq_kv + BKV - 1) / BKV;
     if (CAUSAL) nkv = min(nkv, (min(a.seq_q, q0 + BQ) - 1) / BKV + 1);  // keys beyond the block's last query
 
-    f32x16 o[DB];
+    f32x16 o[QG][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float m = -__builtin_inff();  // running max of the log2-scaled scores of my_q
-    float l = 0.0f;               // running sum of this lane's weights (its half of the keys)
-
-    // One key block: scores, online softmax update, O^T += V^T P^T. The stage
-    // pointers never alias the stage being filled (restrict keeps the
-    // compiler from waiting on those loads before reading these).
-    auto block = [&](const char *__restrict__ kt, const char *__restrict__ vt, int kv0) {
-        f32x16 s[SB];
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[sb][r] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < DK; ++kk)
-                s[sb] = Mfma<TI>::run(frag_from_ktile<BKV, D>(kt, 32 * sb, 16 * kk, lane), qf[kk], s[sb]);
-        }
-        float mb = -__builtin_inff();
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + 32 * sb + 16 * (r >> 3) + 8 * half + (r & 7);
-                float t = s[sb][r] * a.scale_log2;
-                if (key >= a.seq_kv || (CAUSAL && key > my_q)) t = -__builtin_inff();
-                s[sb][r] = t;
-                mb = fmaxf(mb, t);
-            }
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const float mn = fmaxf(m, mb);
-        const float mu = mn == -__builtin_inff() ? 0.0f : mn;  // nothing allowed yet: weights stay 0
-        const float alpha = __builtin_amdgcn_exp2f(m - mu);
-        float ps = 0.0f;
-        u32x4 pf[PT];
-#pragma unroll
-        for (int t = 0; t < PT; ++t) {
-            uint16_t e8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + e] - mu);
-                ps += p;
-                e8[e] = from_f32<TI>(p);
-            }
-            pf[t] = pack8(e8);
-        }
-        l = l * alpha + ps;
-        m = mn;
+    for (int g = 0; g < QG; ++g)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            for (int r = 0; r < 16; ++r) o[g][db][r] = 0.0f;
+    float m[QG], l[QG];  // running max of the log2-scaled scores; this lane's running sum (its half of the keys)
+#pragma unroll
+    for (int g = 0; g < QG; ++g) m[g] = -__builtin_inff(), l[g] = 0.0f;
+
+    // Scores of one key block: S^T = K Q^T for the wave's query groups.
+    auto qk = [&](const char *__restrict__ kt, f32x16 (&s)[QG][SB]) {
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+#pragma unroll
+            for (int g = 0; g < QG; ++g)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[g][sb][r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk) {
+                const u32x4 kf = frag_from_ktile<BKV, D>(kt, 32 * sb, 16 * kk, lane);
+#pragma unroll
+                for (int g = 0; g < QG; ++g) s[g][sb] = Mfma<TI>::run(kf, qf[g][kk], s[g][sb]);
+            }
+        }
+    };
+
+    // Online softmax update of one key block's scores, then O^T += V^T P^T.
+    // MASK: the block holds keys past seq_kv or past some query of the wave
+    // (causal); interior blocks skip the per-score test.
+    auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[QG][SB], const char *__restrict__ vt, int kv0) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        u32x4 pf[QG][PT];
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            // The max is taken on the raw scores (scale > 0 keeps their
+            // order); the scale folds into the exponent's fused multiply-add.
+            float mb = -__builtin_inff();
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if constexpr (MASK) {
+                        const int key = kv0 + 32 * sb + 16 * (r >> 3) + 8 * half + (r & 7);
+                        if (key >= a.seq_kv || (CAUSAL && key > my_q[g])) s[g][sb][r] = -__builtin_inff();
+                    }
+                    mb = fmaxf(mb, s[g][sb][r]);
+                }
+            mb = fmaxf(mb, __shfl_xor(mb, 32)) * a.scale_log2;
+            const float mn = fmaxf(m[g], mb);
+            const float mu = mn == -__builtin_inff() ? 0.0f : mn;  // nothing allowed yet: weights stay 0
+            float ps = 0.0f;
+#pragma unroll
+            for (int t = 0; t < PT; ++t) {
+                uint16_t e8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][t >> 1][8 * (t & 1) + e], a.scale_log2, -mu));
+                    ps += p;
+                    e8[e] = from_f32<TI>(p);
+                }
+                pf[g][t] = pack8(e8);
+            }
+            // Rescale what was accumulated only when some lane's max grew.
+            if (__any(mn != m[g])) {
+                const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
+                l[g] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[g][db][r] *= alpha;
+            }
+            l[g] += ps;
+            m[g] = mn;
+        }
 #pragma unroll
         for (int t = 0; t < PT; ++t)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                o[db] = Mfma<TI>::run(frag_from_rtile<D, BKV>(vt, 32 * db, 16 * t, lane), pf[t], o[db]);
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 vf = frag_from_rtile<D, BKV>(vt, 32 * db, 16 * t, lane);
+#pragma unroll
+                for (int g = 0; g < QG; ++g) o[g][db] = Mfma<TI>::run(vf, pf[g][t], o[g][db]);
+            }
     };
 
+    // A whole key block; each branch of the mask test gets its own copy
+    // (sharing the score products ahead of the branch raised the register
+    // count from 164 to 220).
+    auto block = [&](auto mask_tag, const char *__restrict__ kt, const char *__restrict__ vt, int kv0) {
+        f32x16 sc[QG][SB];
+        qk(kt, sc);
+        softmax_pv(mask_tag, sc, vt, kv0);
+    };
+
+    // One barrier per key block. (Issuing the next block's score products
+    // before this block's softmax -- a software pipeline -- needs a second
+    // score register set: 252 registers, two waves per SIMD, measured 10%
+    // slower than this loop at 164 registers and three waves per SIMD.)
+    // The stage pointers never alias the stage being filled (restrict keeps
+    // the compiler from waiting on those loads before reading these).
+    const int last_q = wq0 + 32 * QG - 1;  // causal: blocks past it add nothing for this wave
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) issue(lds + s * STAGE, s * BKV);
     int cur = 0;
@@ -182,36 +233,43 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         const int fill = cur == 0 ? S - 1 : cur - 1;
         issue(lds + fill * STAGE, (kb + S - 1) * BKV);
         const int kv0 = kb * BKV;
-        // causal: a wave whose queries all precede the block has nothing to add
-        if (!CAUSAL || kv0 <= wq0 + 31) block(lds + cur * STAGE, lds + cur * STAGE + K_BYTES, kv0);
+        const char *kt = lds + cur * STAGE;
+        if (!CAUSAL || kv0 <= last_q) {
+            const bool mask = kv0 + BKV > a.seq_kv || (CAUSAL && kv0 + BKV - 1 > wq0);
+            if (mask) block(std::true_type{}, kt, kt + K_BYTES, kv0);
+            else block(std::false_type{}, kt, kt + K_BYTES, kv0);
+        }
         cur = cur + 1 == S ? 0 : cur + 1;
     }
     wait_vmcnt<0>();  // the trailing out-of-range loads land before the workgroup exits
 
-    // O = O^T / l (lane l holds query my_q, head_dim rows 32db + 8*(r/4) + 4*(l/32) + r%4)
-    const float lt = l + __shfl_xor(l, 32);
-    if (my_q >= a.seq_q) return;
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    // O = O^T / l (lane l holds query my_q[g], head_dim rows 32db + 8*(r/4) + 4*(l/32) + r%4)
     char *Op = static_cast<char *>(a.O);
     const int es = a.out_dtype == DG_F32 ? 4 : 2;
-    const int64_t orow = ((int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)my_q * a.os) * es;
-    const bool vec = (((uintptr_t)Op + orow) % (uintptr_t)(4 * es)) == 0;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int g = 0; g < QG; ++g) {
+        const float lt = l[g] + __shfl_xor(l[g], 32);
+        if (my_q[g] >= a.seq_q) continue;
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        const int64_t orow = ((int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)my_q[g] * a.os) * es;
+        const bool vec = (((uintptr_t)Op + orow) % (uintptr_t)(4 * es)) == 0;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d0 = 32 * db + 8 * r4 + 4 * half;
-            float y[4];
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = o[db][4 * r4 + e] * inv;
-            char *p = Op + orow + (int64_t)d0 * es;
-            if (a.out_dtype == DG_F32) store4_t<DG_F32>(p, vec, 4, 1, y);
-            else if (a.out_dtype == DG_BF16) store4_t<DG_BF16>(p, vec, 4, 1, y);
-            else store4_t<DG_F16>(p, vec, 4, 1, y);
-        }
-    if (a.lse && half == 0)
-        a.lse[((int64_t)b * a.heads + h) * a.seq_q + my_q] =
-            lt > 0.0f ? (m + __log2f(lt)) * 0.69314718055994530942f : -__builtin_inff();
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * db + 8 * r4 + 4 * half;
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = o[g][db][4 * r4 + e] * inv;
+                char *p = Op + orow + (int64_t)d0 * es;
+                if (a.out_dtype == DG_F32) store4_t<DG_F32>(p, vec, 4, 1, y);
+                else if (a.out_dtype == DG_BF16) store4_t<DG_BF16>(p, vec, 4, 1, y);
+                else store4_t<DG_F16>(p, vec, 4, 1, y);
+            }
+        if (a.lse && half == 0)
+            a.lse[((int64_t)b * a.heads + h) * a.seq_q + my_q[g]] =
+                lt > 0.0f ? (m[g] + __log2f(lt)) * 0.69314718055994530942f : -__builtin_inff();
+    }
 }
 
 template <typename TI, int D, bool CAUSAL>

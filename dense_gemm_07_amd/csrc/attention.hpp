@@ -21,9 +21,12 @@ struct AttnArgs {
     int32_t causal;
 };
 
-constexpr int kAttnBlockQ = 128;  // queries per workgroup (4 waves x 32)
-constexpr int kAttnBlockKV = 64;  // keys per step
-constexpr int kAttnStages = 3;    // K/V blocks in the LDS ring
+// One 32-query group per wave measured best: two groups (sharing each K/V
+// fragment read) need 256+ registers, one wave per SIMD, and ran 19% slower.
+constexpr int kAttnQueryGroups = 1;  // 32-query groups per wave
+constexpr int kAttnBlockQ = 128;     // queries per workgroup (4 waves x groups x 32)
+constexpr int kAttnBlockKV = 64;     // keys per step
+constexpr int kAttnStages = 3;       // K/V blocks in the LDS ring
 
 // Launches the kernel for an input dtype / head_dim pair; hipErrorInvalidValue
 // if none is compiled.
