@@ -149,7 +149,7 @@ def bench_attention(args):
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["bf16"]
     result = {
-        "metric": "attention forward TFLOP/s (bf16, seq 8192, head_dim 64) on 1 MI355X",
+        "metric": f"attention forward TFLOP/s (bf16, seq {S}, head_dim {D}) on 1 MI355X",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",

@@ -43,13 +43,19 @@ template <typename TI, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     constexpr int NW = 4;
     constexpr int QG = kAttnQueryGroups;  // 32-query groups per wave
-    constexpr int BQ = kAttnBlockQ, BKV = kAttnBlockKV, S = kAttnStages;
+    constexpr int BQ = kAttnBlockQ, BKV = kAttnBlockKV, S = attn_stages(D);
     static_assert(BQ == NW * 32 * QG, "QG 32-query column blocks per wave");
-    using KT = KTile<BKV, D>;  // K block: rows = keys (permuted), k = head_dim
-    using VT = RTile<D, BKV>;  // V block: k = keys, rows = head_dim
-    constexpr int K_BYTES = BKV * D * 2, STAGE = 2 * BKV * D * 2;
-    constexpr int K_PER = KT::NLOADS / NW, V_PER = VT::NLOADS / NW;
-    static_assert(KT::NLOADS % NW == 0 && VT::NLOADS % NW == 0, "loads split evenly over the waves");
+    static_assert(D % 64 == 0, "head_dim in whole 64-column K tiles");
+    // K block: rows = keys (permuted), k = head_dim, stored as D/64 tiles of
+    // 64 columns (the tile format's rows are 128 bytes). V block: k = keys,
+    // rows = head_dim.
+    constexpr int KH = D / 64;
+    using KT = KTile<BKV, 64>;
+    using VT = RTile<D, BKV>;
+    constexpr int K_HALF = BKV * 64 * 2;  // bytes of one 64-column K tile
+    constexpr int K_BYTES = KH * K_HALF, STAGE = 2 * BKV * D * 2;
+    constexpr int K_PER = KH * KT::NLOADS / NW, V_PER = VT::NLOADS / NW;
+    static_assert((KH * KT::NLOADS) % NW == 0 && VT::NLOADS % NW == 0, "loads split evenly over the waves");
     constexpr int LOADS = K_PER + V_PER;  // per wave and key block
     constexpr int DK = D / 16;            // k-steps of K Q^T
     constexpr int DB = D / 32;            // 32-row blocks of O^T
@@ -90,10 +96,11 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     int kkey[K_PER], kvo[K_PER], vkey[V_PER], vvo[V_PER];
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
+        const int bl = wave + NW * j;  // wave load bl fills 1 KiB at byte bl * 1024: tile bl / NLOADS
         int row, k;
-        KT::src(wave + NW * j, lane, row, k);
+        KT::src(bl % KT::NLOADS, lane, row, k);
         kkey[j] = attn_key_of_row(row);
-        kvo[j] = (int)(2 * ((int64_t)kkey[j] * a.ks + k));
+        kvo[j] = (int)(2 * ((int64_t)kkey[j] * a.ks + 64 * (bl / KT::NLOADS) + k));
     }
 #pragma unroll
     for (int j = 0; j < V_PER; ++j) {
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
                 for (int r = 0; r < 16; ++r) s[g][sb][r] = 0.0f;
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
-                const u32x4 kf = frag_from_ktile<BKV, D>(kt, 32 * sb, 16 * kk, lane);
+                const u32x4 kf = frag_from_ktile<BKV, 64>(kt + (kk / 4) * K_HALF, 32 * sb, 16 * (kk % 4), lane);
 #pragma unroll
                 for (int g = 0; g < QG; ++g) s[g][sb] = Mfma<TI>::run(kf, qf[g][kk], s[g][sb]);
             }
@@ -278,17 +285,18 @@ static void launch_t(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd<TI, D, CAUSAL>), dim3(groups), dim3(256), 0, s, a);
 }
 
+template <typename TI, int D>
+static void launch_d(const AttnArgs &a, hipStream_t s) {
+    if (a.causal) launch_t<TI, D, true>(a, s);
+    else launch_t<TI, D, false>(a, s);
+}
+
 hipError_t launch_attention(const AttnArgs &a, int in_dtype, int head_dim, hipStream_t s) {
-    if (head_dim != 64) return hipErrorInvalidValue;
-    if (in_dtype == DG_BF16) {
-        if (a.causal) launch_t<BF16, 64, true>(a, s);
-        else launch_t<BF16, 64, false>(a, s);
-    } else if (in_dtype == DG_F16) {
-        if (a.causal) launch_t<F16, 64, true>(a, s);
-        else launch_t<F16, 64, false>(a, s);
-    } else {
-        return hipErrorInvalidValue;
-    }
+    if (in_dtype != DG_BF16 && in_dtype != DG_F16) return hipErrorInvalidValue;
+    const bool bf = in_dtype == DG_BF16;
+    if (head_dim == 64) bf ? launch_d<BF16, 64>(a, s) : launch_d<F16, 64>(a, s);
+    else if (head_dim == 128) bf ? launch_d<BF16, 128>(a, s) : launch_d<F16, 128>(a, s);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

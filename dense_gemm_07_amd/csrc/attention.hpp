@@ -26,7 +26,11 @@ struct AttnArgs {
 constexpr int kAttnQueryGroups = 1;  // 32-query groups per wave
 constexpr int kAttnBlockQ = 128;     // queries per workgroup (4 waves x groups x 32)
 constexpr int kAttnBlockKV = 64;     // keys per step
-constexpr int kAttnStages = 3;       // K/V blocks in the LDS ring
+constexpr int kAttnStages = 3;       // most K/V blocks in the LDS ring (head_dim 64)
+
+// K/V blocks in the LDS ring for a head_dim: 3 x 16 KiB at 64; 2 x 32 KiB at
+// 128 (two workgroups per CU instead of one).
+constexpr int attn_stages(int head_dim) { return head_dim <= 64 ? 3 : 2; }
 
 // Launches the kernel for an input dtype / head_dim pair; hipErrorInvalidValue
 // if none is compiled.

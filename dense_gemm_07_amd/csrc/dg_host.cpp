@@ -751,7 +751,8 @@ dg_status dg_attention_fwd(int64_t batch, int64_t heads, int64_t seq_q, int64_t 
         for (int i = 0; i < 3; ++i)
             if (st[i] < 0) return fail(DG_ERR_INVALID_VALUE, "negative stride");
     if (in_dtype == DG_F32) return fail(DG_ERR_UNSUPPORTED, "attention takes fp16 or bf16 Q, K, V");
-    if (head_dim != 64) return fail(DG_ERR_UNSUPPORTED, "head_dim %" PRId64 " (supported: 64)", head_dim);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(DG_ERR_UNSUPPORTED, "head_dim %" PRId64 " (supported: 64, 128)", head_dim);
     // O's rows must not overlap: (batch, head, seq, dim) strides nested when sorted.
     if (!nested({{batch, o_strides[0]}, {heads, o_strides[1]}, {seq_q, o_strides[2]}, {head_dim, 1}}))
         return fail(DG_ERR_INVALID_VALUE, "O strides make its elements overlap");

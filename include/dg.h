@@ -287,7 +287,7 @@ dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count
  *  Numerics: fp32 scores, softmax and accumulation; the softmax weights are
  *     rounded to in_dtype for the product with V (the matrix cores take 16-bit
  *     operands); the normalising sum uses the unrounded weights.
- *  Supported: head_dim 64. Other head_dim values, in_dtype f32, or layouts
+ *  Supported: head_dim 64 and 128. Other head_dim values, in_dtype f32, or layouts
  *     outside the above return DG_ERR_UNSUPPORTED; bad arguments return
  *     DG_ERR_INVALID_VALUE. Any size may be 0 (nothing to do; seq_kv == 0
  *     writes O = 0 and lse = -inf). seq_q, seq_kv < 2^30.

@@ -97,6 +97,18 @@ def test_attention_random(shape, causal, dtype, out_dtype):
     check(q, k, v, dtype, out_dtype, causal, what=f"{shape} causal={causal} {dtype}->{out_dtype}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (2, 3, 100, 77), (1, 2, 300, 513), (1, 1, 64, 2048)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype,out_dtype", [("bf16", "bf16"), ("f16", "f32")])
+def test_attention_head_dim_128(shape, causal, dtype, out_dtype):
+    B, H, Sq, Skv = shape
+    q, k, v = (draw((B, H, s, 128), dtype, seed) for s, seed in ((Sq, 21), (Skv, 22), (Skv, 23)))
+    check(q, k, v, dtype, out_dtype, causal, what=f"d128 {shape} causal={causal} {dtype}->{out_dtype}")
+    if shape == (2, 3, 100, 77):  # interleaved heads at d = 128 too
+        check(q, k, v, dtype, out_dtype, causal, kinds=("bshd", "bshd", "bshd"), what="d128 bshd")
+
+
 @pytest.mark.parametrize("kinds", [("bshd", "bshd", "bshd"), ("bhsd", "bshd", "bhsd")])
 def test_attention_interleaved_heads(kinds):
     q, k, v = (draw((2, 4, s, 64), "bf16", seed) for s, seed in ((190, 4), (333, 5), (333, 6)))
@@ -167,6 +179,16 @@ def test_attention_full_size_sampled():
         assert np.all(np.abs(got - ref) <= tol), f"causal={causal} max err {np.abs(got - ref).max()}"
         gl = lse[:, :, rows].double().cpu().numpy()
         assert np.all(np.abs(gl - ref_lse) <= 1e-4 * (1 + np.abs(ref_lse)))
+
+
+def test_attention_zero_queries_average_values_d128():
+    q = torch.zeros(1, 1, 130, 128, dtype=torch.float16)
+    k, v = draw((1, 1, 130, 128), "f16", 24), draw((1, 1, 130, 128), "f16", 25)
+    o = dg.attention(q.to(DEV), k.to(DEV), v.to(DEV), out_dtype=torch.float32, causal=True)
+    torch.cuda.synchronize()
+    vv = v.double().numpy()
+    for i in (0, 63, 64, 129):
+        assert np.allclose(o[:, :, i].double().cpu().numpy(), vv[:, :, :i + 1].mean(axis=2), rtol=0, atol=3e-6)
 
 
 def test_attention_rejects_unsupported():

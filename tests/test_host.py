@@ -341,7 +341,7 @@ def test_attention_argument_checks():
     UNSUPPORTED = 2
     assert attn_status(B=-1) == INVALID
     assert attn_status(q=None) == INVALID
-    assert attn_status(D=128) == UNSUPPORTED and b"head_dim" in dg.library().dg_last_error()
+    assert attn_status(D=96) == UNSUPPORTED and b"head_dim" in dg.library().dg_last_error()
     assert attn_status(dt=F32) == UNSUPPORTED
     assert attn_status(q=FAKE + 2) == UNSUPPORTED           # Q not 16-byte aligned
     assert attn_status(st=(512, 512, 66)) == UNSUPPORTED    # seq stride not a multiple of 8
