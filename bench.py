@@ -183,6 +183,10 @@ def main():
     ap.add_argument("--batch", type=int, default=1, help="time a strided batch of this many products (dg_gemm_ex)")
     ap.add_argument("--split-k", action="store_true",
                     help="time dg_gemm_ex with a workspace (the library may split K)")
+    ap.add_argument("--config", default="",
+                    help="time an explicit kernel config BMxBNxBK:waves:stages:group_m:xcd_remap (ablations)")
+    ap.add_argument("--misalign-a", action="store_true",
+                    help="view A one element past a 16-byte boundary (forces the register-staged kernel)")
     ap.add_argument("--attention", action="store_true",
                     help="time the attention forward kernel instead (--batch, --heads, --seq, --head-dim, --causal)")
     ap.add_argument("--heads", type=int, default=16)
@@ -233,6 +237,11 @@ def main():
         a = inputs.to_device_like(a_cpu, dev)
         b = inputs.to_device_like(b_cpu, dev)
         c = torch.empty((w.M, w.N), dtype=out_dt, device=dev)
+        if args.misalign_a:
+            buf = torch.empty(a.numel() + 1, dtype=a.dtype, device=dev)
+            view = buf[1:].view(a.shape)
+            view.copy_(a)
+            a = view
     # Epilogue operands (seeded): an fp32 bias per column, or a residual of C's dtype.
     gen = torch.Generator().manual_seed(1)
     epi = {}
@@ -252,7 +261,19 @@ def main():
         t0 = time.perf_counter()
         cfg, _ = dg.autotune(a, b, out=c, repeats=10)
         tune_s = time.perf_counter() - t0
-    if ex:
+    explicit = None
+    if args.config:
+        shape, waves, stages, group_m, xcd = args.config.split(":")
+        bm, bn, bk = (int(x) for x in shape.split("x"))
+        explicit = next((k for k in dg.candidates(dg._dtype_code(a.dtype), dg._dtype_code(c.dtype))
+                         if (k.block_m, k.block_n, k.block_k, k.waves, k.stages) ==
+                         (bm, bn, bk, int(waves), int(stages))), None)
+        if explicit is None:
+            raise SystemExit(f"no compiled kernel {args.config}")
+        explicit.group_m, explicit.xcd_remap, explicit.k_splits = int(group_m), int(xcd), 1
+    if explicit is not None:
+        cfg = explicit
+    elif ex:
         ws_bytes = dg.DEFAULT_WORKSPACE_BYTES if args.split_k else 0
         cfg, _ = dg.select_config_ex(w.M, w.N, w.K, a.stride()[-2:], b.stride()[-2:], c.stride()[-2:],
                                      dg._dtype_code(a.dtype), dg._dtype_code(c.dtype), batch=nb,
@@ -264,9 +285,12 @@ def main():
     print(f"# workload {w.name}: config {cfg} (autotune {tune_s:.2f} s)", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
-    if ex:
+    if explicit is not None and not ex:
         def step():
-            dg.gemm_ex(a, b, out=c, stream=stream, workspace=True if args.split_k else None, **epi)
+            dg.gemm_config(a, b, explicit, out=c, stream=stream)
+    elif ex:
+        def step():
+            dg.gemm_ex(a, b, out=c, stream=stream, workspace=True if args.split_k else None, config=explicit, **epi)
     else:
         def step():
             dg.gemm(a, b, out=c, stream=stream)
@@ -316,7 +340,10 @@ def main():
     }
     if ex:
         result["config"].update({"epilogue": args.epilogue, "batch": nb, "split_k_allowed": args.split_k})
-    if not args.no_cpu_baseline and not ex:
+    if args.config or args.misalign_a:
+        result["config"].update({"explicit_config": args.config, "misaligned_a": args.misalign_a})
+        result["roofline"]["traffic"] = None  # the recorded counters belong to the default configuration
+    if not args.no_cpu_baseline and not ex and not args.config and not args.misalign_a:
         result["cpu_baseline"] = cpu_baseline(w, a_cpu, b_cpu)
     print(json.dumps(result), flush=True)
 
