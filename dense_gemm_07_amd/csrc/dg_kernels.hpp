@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dg_internal.hpp"
 
 namespace dg {
@@ -922,8 +924,10 @@ struct DirectLoader {
     }
 
     // Queue the tile of k-slice [k0, k0 + BK) into `tile` (this wave's share).
+    // MASK_K = false: the caller knows the slice lies inside K (no k mask).
+    template <bool MASK_K = true>
     __device__ __forceinline__ void issue(char *tile, int k0, int K, int wave, int lane) const {
-        const bool tail = k0 + BK > K;
+        const bool tail = MASK_K && k0 + BK > K;
         const int soff = k0 * kstride_bytes;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -1084,9 +1088,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
 #pragma unroll
         for (int t = from; t < to; ++t) acc[t / FN][t % FN] = Mfma<TI>::run(af[set][t / FN], bf[set][t % FN], acc[t / FN][t % FN]);
     };
-    auto step = [&](char *fill, const char *__restrict__ cur, const char *next, int kt) {
-        la.issue(fill, (kt + S - 1) * BK, kl, wave, lane);
-        lb.issue(fill + A_BYTES, (kt + S - 1) * BK, kl, wave, lane);
+    auto step = [&](auto mask_k, char *fill, const char *__restrict__ cur, const char *next, int kt) {
+        constexpr bool MASK_K = decltype(mask_k)::value;
+        la.template issue<MASK_K>(fill, (kt + S - 1) * BK, kl, wave, lane);
+        lb.template issue<MASK_K>(fill + A_BYTES, (kt + S - 1) * BK, kl, wave, lane);
 #pragma unroll
         for (int kk = 0; kk + 1 < KSUB; ++kk) {
             fetch(cur, kk + 1, (kk & 1) ^ 1);
@@ -1109,12 +1114,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
         sched_fence();
     };
     static_assert(KSUB % 2 == 0, "substep 0 of every slice uses fragment set 0");
-    int cur = 0;
-    for (int kt = 0; kt < nk; ++kt) {
+    // Slice kt lives in stage kt % S. Steps whose prefetched slice kt+S-1 lies
+    // inside K (kt < n_full) need no k mask; they run S at a time, so every
+    // stage address is a compile-time offset and the loop carries no address
+    // or mask arithmetic. The last steps (at most S-1 + S-1 of them) run with
+    // the stage chosen at run time and the masked loads.
+    const int n_full = max(0, min(nk, kl / BK - (S - 1)));
+    int kt = 0;
+    for (; kt + S <= n_full; kt += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u)
+            step(std::false_type{}, lds + ((u + S - 1) % S) * STAGE, lds + u * STAGE, lds + ((u + 1) % S) * STAGE,
+                 kt + u);
+    }
+    for (; kt < nk; ++kt) {
+        const int cur = kt % S;
         const int fill = cur == 0 ? S - 1 : cur - 1;  // stage of slice kt-1 == slice kt+S-1
         const int next = cur + 1 == S ? 0 : cur + 1;
-        step(lds + fill * STAGE, lds + cur * STAGE, lds + next * STAGE, kt);
-        cur = next;
+        step(std::true_type{}, lds + fill * STAGE, lds + cur * STAGE, lds + next * STAGE, kt);
     }
     wait_vmcnt<0>();  // the out-of-range tail loads must land before the workgroup can exit
 
