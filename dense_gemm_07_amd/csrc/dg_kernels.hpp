@@ -449,6 +449,7 @@ struct EpiRows {
     char *C;                 // C of this product (bytes)
     int c_es;
     bool cvec, rvec, use_r;
+    int rmode;               // residual words as loaded: 0 four fp32, 1 four bf16, 2 four fp16
     int64_t r_off, b_off;
     float bcol[4];           // per-column bias of the group (0 if none)
     bool row_bias;
@@ -482,77 +483,104 @@ __device__ __forceinline__ void store4_t(char *p, bool vec, int n, int64_t s, co
     }
 }
 
+// Issues the residual and per-row bias loads of this thread's RU rows of one
+// pass (rows r0, r0 + rs, ...). Nothing waits for them here: the caller
+// stages the accumulators meanwhile, so one memory latency per pass is
+// exposed instead of one per few rows. A row's 4 residual elements are one
+// 8- or 16-byte load when rvec (rmode 1/2: raw 16-bit pairs; rmode 0: fp32
+// words), else element loads converted to fp32 (rmode 0).
+template <int RU>
+__device__ __forceinline__ void epi_load(const GemmArgs &g, const EpiRows &e, uint32_t (&raw)[RU][4],
+                                         float (&br)[RU]) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        const int row = e.r0 + u * e.rs;
+        const bool in = row < e.rows;
+        const int gm = e.m_row0 + row;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) raw[u][k] = 0u;
+        if (in && e.use_r) {
+            const int64_t off = e.r_off + (int64_t)gm * g.srm + e.gn0;
+            if (e.rvec && e.rmode == 0) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const float *>(g.R) + off);
+                raw[u][0] = v.x, raw[u][1] = v.y, raw[u][2] = v.z, raw[u][3] = v.w;
+            } else if (e.rvec) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g.R) + off);
+                raw[u][0] = v.x, raw[u][1] = v.y;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (k < e.ncols)
+                        raw[u][k] = __float_as_uint(load_any(g.R, off - e.gn0 + (int64_t)(e.gn0 + k) * g.srn, g.r_dtype));
+            }
+        }
+        br[u] = (in && e.row_bias) ? load_any(g.bias, e.b_off + (int64_t)gm * g.sbias, g.bias_dtype) : 0.0f;
+    }
+}
+
 // The staged rows of one pass through act(alpha*x + beta*R + bias), for one
 // activation and output dtype (so the per-element work has no branches: an
 // absent residual or bias enters as +0, which changes at most the sign of a
-// zero result). The residual and per-row bias loads of U rows are issued
-// before any of them is used: the loop is otherwise bound by their latency.
-template <int ACT, int OUT, int U>
-__device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e) {
-#pragma unroll 1
-    for (int rr = e.r0; rr < e.rows; rr += U * e.rs) {
-        float rv[U][4], br[U];
+// zero result).
+template <int ACT, int OUT, int RU>
+__device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, const uint32_t (&raw)[RU][4],
+                                         const float (&br)[RU]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {  // issue the global loads of U rows first
-            const int row = rr + u * e.rs;
-            const bool in = row < e.rows;
-            const int gm = e.m_row0 + row;
+    for (int u = 0; u < RU; ++u) {
+        const int row = e.r0 + u * e.rs;
+        if (row >= e.rows) continue;
+        float rv[4];
+        if (e.rmode == 0) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) rv[u][k] = 0.0f;
-            if (in && e.use_r) {
-                const int64_t off = e.r_off + (int64_t)gm * g.srm;
-                if (g.srn == 1) {
-                    load4(g.R, off + e.gn0, g.r_dtype, e.rvec, e.ncols, rv[u]);
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (k < e.ncols) rv[u][k] = load_any(g.R, off + (int64_t)(e.gn0 + k) * g.srn, g.r_dtype);
-                }
-            }
-            br[u] = (in && e.row_bias) ? load_any(g.bias, e.b_off + (int64_t)gm * g.sbias, g.bias_dtype) : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int row = rr + u * e.rs;
-            if (row >= e.rows) continue;
-            const float4 v = *reinterpret_cast<const float4 *>(e.st + row * e.ldn + e.c4);
-            const float x[4] = {v.x, v.y, v.z, v.w};
-            float y[4];
+            for (int k = 0; k < 4; ++k) rv[k] = __uint_as_float(raw[u][k]);
+        } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                float t = __builtin_fmaf(g.beta, rv[u][k], g.alpha * x[k]) + (e.bcol[k] + br[u]);
-                if constexpr (ACT == DG_ACT_RELU) t = t < 0.0f ? 0.0f : t;
-                if constexpr (ACT == DG_ACT_GELU) t = activate(t, DG_ACT_GELU);
-                y[k] = t;
+                const uint16_t h = (uint16_t)(raw[u][k >> 1] >> (16 * (k & 1)));
+                rv[k] = e.rmode == 1 ? to_f32<BF16>(h) : to_f32<F16>(h);
             }
-            store4_t<OUT>(e.C + ((int64_t)(e.m_row0 + row) * g.scm + (int64_t)e.gn0 * g.scn) * e.c_es, e.cvec,
-                          e.ncols, g.scn, y);
         }
+        const float4 v = *reinterpret_cast<const float4 *>(e.st + row * e.ldn + e.c4);
+        const float x[4] = {v.x, v.y, v.z, v.w};
+        float y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float t = __builtin_fmaf(g.beta, rv[k], g.alpha * x[k]) + (e.bcol[k] + br[u]);
+            if constexpr (ACT == DG_ACT_RELU) t = t < 0.0f ? 0.0f : t;
+            if constexpr (ACT == DG_ACT_GELU) t = activate(t, DG_ACT_GELU);
+            y[k] = t;
+        }
+        store4_t<OUT>(e.C + ((int64_t)(e.m_row0 + row) * g.scm + (int64_t)e.gn0 * g.scn) * e.c_es, e.cvec, e.ncols,
+                      g.scn, y);
     }
 }
 
 // The same tile through the fused epilogue, staged through LDS. The tile is
 // written to LDS (fp32, rows padded by 4 floats) in passes of whole 32-row
 // fragment blocks. Each thread then owns one 4-column group of the tile
-// (T is a multiple of BN/4) and walks its rows (epi_rows): a per-column bias
-// is loaded once per tile, and a row's 4 elements of C and of the residual
-// move as one vector when the layout allows. `st` is the kernel's LDS (CAP
-// bytes, free: the K loop is done).
+// (T is a multiple of BN/4) and RU rows of each pass: a per-column bias is
+// loaded once per tile, the pass's residual rows are requested before the
+// staging (epi_load), and a row's 4 elements of C and of the residual move as
+// one vector when the layout allows. `st` is the kernel's LDS (CAP bytes,
+// free: the K loop is done).
 template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
 __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
                                           float *st, int m0, int n0) {
     constexpr int T = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int LDN = BN + 4;
-    constexpr int FIT = CAP / 4 / LDN;
-    constexpr int PR = FIT >= BM ? BM : (FIT / 32) * 32;  // rows per pass
-    static_assert(PR >= 32, "LDS too small to stage 32 rows of the tile");
     constexpr int Q = BN / 4;  // 4-column groups per row
     static_assert(T % Q == 0, "every thread keeps one column group");
-    // Rows whose loads are in flight together: 8 where registers allow; 4
-    // for the large tiles, whose 128 accumulators would otherwise push the
-    // register count up enough to change how the K loop is scheduled.
-    constexpr int U = FM * FN >= 8 ? 4 : 8;
+    constexpr int RS = T / Q;  // rows between a thread's rows
+    constexpr int FIT = CAP / 4 / LDN;
+    // Rows per pass: whole 32-row blocks that fit in LDS, and at most 8 rows
+    // per thread with two waves per SIMD (12 with one), which bounds the
+    // registers holding the pass's residual next to the accumulators.
+    constexpr int PR0 = FIT >= BM ? BM : (FIT / 32) * 32;
+    constexpr int PRC = ((T >= 512 ? 8 : 12) * RS) / 32 * 32;
+    constexpr int PR = PR0 < PRC ? PR0 : (PRC >= 32 ? PRC : 32);
+    static_assert(PR >= 32 && PR <= PR0, "LDS too small to stage 32 rows of the tile");
+    constexpr int RU = (PR + RS - 1) / RS;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     EpiRows e;
@@ -560,7 +588,7 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
     e.ldn = LDN;
     e.c4 = (tid % Q) * 4;
     e.r0 = tid / Q;
-    e.rs = T / Q;
+    e.rs = RS;
     e.gn0 = n0 + e.c4;
     e.ncols = min(4, g.N - e.gn0);
     e.c_es = g.out_dtype == DG_F32 ? 4 : 2;
@@ -579,8 +607,14 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
              ((uintptr_t)(e.C + (int64_t)e.gn0 * e.c_es) % (uintptr_t)(4 * e.c_es)) == 0;
     e.rvec = e.ncols == 4 && e.use_r && g.srn == 1 && g.srm % 4 == 0 &&
              ((uintptr_t)g.R + (uintptr_t)((e.r_off + e.gn0) * r_es)) % (uintptr_t)(4 * r_es) == 0;
+    e.rmode = (!e.rvec || r_es == 4) ? 0 : (g.r_dtype == DG_BF16 ? 1 : 2);
+    uint32_t raw[RU][4];
+    float br[RU];
 #pragma unroll 1
     for (int p0 = 0; p0 < BM; p0 += PR) {
+        e.m_row0 = m0 + p0;
+        e.rows = min(PR, g.M - m0 - p0);
+        epi_load<RU>(g, e, raw, br);
         __syncthreads();  // the previous pass (or the K loop) is done with the LDS
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -595,22 +629,20 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
             }
         }
         __syncthreads();
-        e.m_row0 = m0 + p0;
-        e.rows = min(PR, g.M - m0 - p0);
         if (e.ncols <= 0) continue;
         const int out = g.out_dtype;
         if (g.act == DG_ACT_GELU) {
-            if (out == DG_BF16) epi_rows<DG_ACT_GELU, DG_BF16, U>(g, e);
-            else if (out == DG_F16) epi_rows<DG_ACT_GELU, DG_F16, U>(g, e);
-            else epi_rows<DG_ACT_GELU, DG_F32, U>(g, e);
+            if (out == DG_BF16) epi_rows<DG_ACT_GELU, DG_BF16, RU>(g, e, raw, br);
+            else if (out == DG_F16) epi_rows<DG_ACT_GELU, DG_F16, RU>(g, e, raw, br);
+            else epi_rows<DG_ACT_GELU, DG_F32, RU>(g, e, raw, br);
         } else if (g.act == DG_ACT_RELU) {
-            if (out == DG_BF16) epi_rows<DG_ACT_RELU, DG_BF16, U>(g, e);
-            else if (out == DG_F16) epi_rows<DG_ACT_RELU, DG_F16, U>(g, e);
-            else epi_rows<DG_ACT_RELU, DG_F32, U>(g, e);
+            if (out == DG_BF16) epi_rows<DG_ACT_RELU, DG_BF16, RU>(g, e, raw, br);
+            else if (out == DG_F16) epi_rows<DG_ACT_RELU, DG_F16, RU>(g, e, raw, br);
+            else epi_rows<DG_ACT_RELU, DG_F32, RU>(g, e, raw, br);
         } else {
-            if (out == DG_BF16) epi_rows<DG_ACT_NONE, DG_BF16, U>(g, e);
-            else if (out == DG_F16) epi_rows<DG_ACT_NONE, DG_F16, U>(g, e);
-            else epi_rows<DG_ACT_NONE, DG_F32, U>(g, e);
+            if (out == DG_BF16) epi_rows<DG_ACT_NONE, DG_BF16, RU>(g, e, raw, br);
+            else if (out == DG_F16) epi_rows<DG_ACT_NONE, DG_F16, RU>(g, e, raw, br);
+            else epi_rows<DG_ACT_NONE, DG_F32, RU>(g, e, raw, br);
         }
     }
 }
@@ -1036,7 +1068,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     constexpr int NLW = NW >= 8 ? NW / 2 : NW;
     using LoaderA = DirectLoader<BM, BK, LA, NLW>;
     using LoaderB = DirectLoader<BN, BK, LB, NLW>;
-    const bool loader = wave < NLW;
+    const bool loader = NLW == NW || wave < NLW;
     constexpr int LOADS_PER_SLICE = LoaderA::PER + LoaderB::PER;  // per loading wave
     LoaderA la;
     LoaderB lb;
