@@ -187,6 +187,8 @@ def main():
                     help="time an explicit kernel config BMxBNxBK:waves:stages:group_m:xcd_remap (ablations)")
     ap.add_argument("--misalign-a", action="store_true",
                     help="view A one element past a 16-byte boundary (forces the register-staged kernel)")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch.matmul (the ROCm vendor GEMM) on the same operands, for context")
     ap.add_argument("--attention", action="store_true",
                     help="time the attention forward kernel instead (--batch, --heads, --seq, --head-dim, --causal)")
     ap.add_argument("--heads", type=int, default=16)
@@ -343,6 +345,25 @@ def main():
     if args.config or args.misalign_a:
         result["config"].update({"explicit_config": args.config, "misaligned_a": args.misalign_a})
         result["roofline"]["traffic"] = None  # the recorded counters belong to the default configuration
+    if args.vendor and not ex and nb == 1:
+        # Context only: the vendor library on the same operands and stream, same step count.
+        # torch.matmul writes the inputs' dtype; where C's dtype differs, it writes a buffer of that dtype.
+        vout = c if c.dtype == a.dtype else torch.empty(c.shape, dtype=a.dtype, device=dev)
+
+        def vstep():
+            torch.matmul(a, b, out=vout)
+        for _ in range(args.warmup):
+            vstep()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            vstep()
+        end.record(stream)
+        torch.cuda.synchronize()
+        vms = start.elapsed_time(end) / args.steps
+        result["vendor"] = {"library": "torch.matmul (hipBLASLt)", "value": round(flops / (vms * 1e-3) / 1e12, 2),
+                            "unit": "TFLOP/s", "ms_per_step": round(vms, 5), "speedup_of_ours": round(vms / ms, 4),
+                            "out_dtype": str(vout.dtype).replace("torch.", "")}
     if not args.no_cpu_baseline and not ex and not args.config and not args.misalign_a:
         result["cpu_baseline"] = cpu_baseline(w, a_cpu, b_cpu)
     print(json.dumps(result), flush=True)
