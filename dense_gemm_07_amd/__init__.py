@@ -118,42 +118,66 @@ def _check(status):
         raise DGError(status, library().dg_last_error().decode(errors="replace"))
 
 
+_DTYPE_CODES = None
+
+
 def _dtype_code(dt):
-    import torch
-    codes = {torch.float32: DG_F32, torch.float16: DG_F16, torch.bfloat16: DG_BF16}
-    if dt not in codes:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: DG_F32, torch.float16: DG_F16, torch.bfloat16: DG_BF16}
+    code = _DTYPE_CODES.get(dt)
+    if code is None:
         raise TypeError(f"unsupported dtype {dt}; use float32, float16 or bfloat16")
-    return codes[dt]
+    return code
 
 
 def _problem(a, b, out):
-    """Marshal (A, B, C) tensors into the C-ABI problem arguments."""
+    """Marshal (A, B, C) tensors into the C-ABI problem arguments.
+
+    This runs on every call, so it reads each tensor property once: for small
+    products the host time of the call is the whole cost."""
     if a.dim() != 2 or b.dim() != 2 or out.dim() != 2:
         raise ValueError("gemm takes 2-D tensors")
     M, K = a.shape
     K2, N = b.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: A is {tuple(a.shape)}, B is {tuple(b.shape)}")
-    if tuple(out.shape) != (M, N):
+    if out.shape[0] != M or out.shape[1] != N:
         raise ValueError(f"out must be {(M, N)}, got {tuple(out.shape)}")
-    if a.dtype != b.dtype:
-        raise TypeError(f"A and B must share a dtype ({a.dtype} vs {b.dtype})")
-    for name, t in (("A", a), ("B", b), ("out", out)):
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
-    return [M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0), b.stride(1),
-            out.data_ptr(), out.stride(0), out.stride(1), _dtype_code(a.dtype), _dtype_code(out.dtype)]
+    in_dt = a.dtype
+    if in_dt != b.dtype:
+        raise TypeError(f"A and B must share a dtype ({in_dt} vs {b.dtype})")
+    if not (a.is_cuda and b.is_cuda and out.is_cuda):
+        raise ValueError("A, B and out must be GPU tensors (there is no CPU path)")
+    sa, sb, so = a.stride(), b.stride(), out.stride()
+    return [M, N, K, a.data_ptr(), sa[0], sa[1], b.data_ptr(), sb[0], sb[1],
+            out.data_ptr(), so[0], so[1], _dtype_code(in_dt), _dtype_code(out.dtype)]
+
+
+_raw_stream = None
 
 
 def _stream(t, stream):
+    """The HIP stream to launch on: `stream`, else torch's current stream on t's device."""
+    global _raw_stream
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_stream is None:
+        import torch
+        # torch's own accessor of the current stream's raw handle (what its
+        # kernel launchers use); the public torch.cuda.current_stream() builds
+        # a Python stream object per call (~2.5 us).
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        return ctypes.c_void_p(_raw_stream(t.get_device()))
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream(t.device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
 def _out(a, b, out, out_dtype):
-    import torch
     if out is None:
+        import torch
         out = torch.empty((a.shape[0], b.shape[1]), dtype=out_dtype or a.dtype, device=a.device)
     return out
 
