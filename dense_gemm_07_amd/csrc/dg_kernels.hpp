@@ -449,7 +449,7 @@ struct EpiRows {
     char *C;                 // C of this product (bytes)
     int c_es;
     bool cvec, rvec, use_r;
-    int rmode;               // residual words as loaded: 0 four fp32, 1 four bf16, 2 four fp16
+    int rmode;               // 16-bit residual requested per pass: 1 bf16, 2 fp16; 0: read at use
     int64_t r_off, b_off;
     float bcol[4];           // per-column bias of the group (0 if none)
     bool row_bias;
@@ -483,61 +483,62 @@ __device__ __forceinline__ void store4_t(char *p, bool vec, int n, int64_t s, co
     }
 }
 
-// Issues the residual and per-row bias loads of this thread's RU rows of one
-// pass (rows r0, r0 + rs, ...). Nothing waits for them here: the caller
-// stages the accumulators meanwhile, so one memory latency per pass is
-// exposed instead of one per few rows. A row's 4 residual elements are one
-// 8- or 16-byte load when rvec (rmode 1/2: raw 16-bit pairs; rmode 0: fp32
-// words), else element loads converted to fp32 (rmode 0).
+// Issues the 16-bit residual loads (one 8-byte vector per row, rmode 1/2)
+// and the per-row bias loads of this thread's RU rows of one pass (rows r0,
+// r0 + rs, ...). Nothing waits for them here: the caller stages the
+// accumulators meanwhile, so one memory latency per pass is exposed instead
+// of one per few rows. An fp32 or unaligned residual (rmode 0) is read where
+// it is used (epi_rows), which keeps two words per row here.
 template <int RU>
-__device__ __forceinline__ void epi_load(const GemmArgs &g, const EpiRows &e, uint32_t (&raw)[RU][4],
+__device__ __forceinline__ void epi_load(const GemmArgs &g, const EpiRows &e, uint32_t (&raw)[RU][2],
                                          float (&br)[RU]) {
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
         const int row = e.r0 + u * e.rs;
         const bool in = row < e.rows;
         const int gm = e.m_row0 + row;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) raw[u][k] = 0u;
-        if (in && e.use_r) {
-            const int64_t off = e.r_off + (int64_t)gm * g.srm + e.gn0;
-            if (e.rvec && e.rmode == 0) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const float *>(g.R) + off);
-                raw[u][0] = v.x, raw[u][1] = v.y, raw[u][2] = v.z, raw[u][3] = v.w;
-            } else if (e.rvec) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g.R) + off);
-                raw[u][0] = v.x, raw[u][1] = v.y;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (k < e.ncols)
-                        raw[u][k] = __float_as_uint(load_any(g.R, off - e.gn0 + (int64_t)(e.gn0 + k) * g.srn, g.r_dtype));
-            }
+        raw[u][0] = raw[u][1] = 0u;
+        if (in && e.rmode != 0) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g.R) + e.r_off +
+                                                             (int64_t)gm * g.srm + e.gn0);
+            raw[u][0] = v.x, raw[u][1] = v.y;
         }
         br[u] = (in && e.row_bias) ? load_any(g.bias, e.b_off + (int64_t)gm * g.sbias, g.bias_dtype) : 0.0f;
     }
 }
 
 // The staged rows of one pass through act(alpha*x + beta*R + bias), for one
-// activation and output dtype (so the per-element work has no branches: an
-// absent residual or bias enters as +0, which changes at most the sign of a
-// zero result).
-template <int ACT, int OUT, int RU>
-__device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, const uint32_t (&raw)[RU][4],
+// activation (so the per-element work has no branches: an absent residual or
+// bias enters as +0, which changes at most the sign of a zero result). The
+// output dtype is a uniform branch per row: one copy of the row code per
+// activation keeps the kernel's code small, and the tile's tail runs once
+// per tile, out of the instruction cache.
+template <int ACT, int RU>
+__device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, const uint32_t (&raw)[RU][2],
                                          const float (&br)[RU]) {
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
         const int row = e.r0 + u * e.rs;
         if (row >= e.rows) continue;
         float rv[4];
-        if (e.rmode == 0) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) rv[k] = __uint_as_float(raw[u][k]);
-        } else {
+        if (e.rmode != 0) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint16_t h = (uint16_t)(raw[u][k >> 1] >> (16 * (k & 1)));
                 rv[k] = e.rmode == 1 ? to_f32<BF16>(h) : to_f32<F16>(h);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rv[k] = 0.0f;
+            if (e.use_r) {
+                const int64_t off = e.r_off + (int64_t)(e.m_row0 + row) * g.srm;
+                if (g.srn == 1) {
+                    load4(g.R, off + e.gn0, g.r_dtype, e.rvec, e.ncols, rv);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (k < e.ncols) rv[k] = load_any(g.R, off + (int64_t)(e.gn0 + k) * g.srn, g.r_dtype);
+                }
             }
         }
         const float4 v = *reinterpret_cast<const float4 *>(e.st + row * e.ldn + e.c4);
@@ -550,8 +551,10 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, co
             if constexpr (ACT == DG_ACT_GELU) t = activate(t, DG_ACT_GELU);
             y[k] = t;
         }
-        store4_t<OUT>(e.C + ((int64_t)(e.m_row0 + row) * g.scm + (int64_t)e.gn0 * g.scn) * e.c_es, e.cvec, e.ncols,
-                      g.scn, y);
+        char *cp = e.C + ((int64_t)(e.m_row0 + row) * g.scm + (int64_t)e.gn0 * g.scn) * e.c_es;
+        if (g.out_dtype == DG_BF16) store4_t<DG_BF16>(cp, e.cvec, e.ncols, g.scn, y);
+        else if (g.out_dtype == DG_F16) store4_t<DG_F16>(cp, e.cvec, e.ncols, g.scn, y);
+        else store4_t<DG_F32>(cp, e.cvec, e.ncols, g.scn, y);
     }
 }
 
@@ -573,14 +576,16 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
     static_assert(T % Q == 0, "every thread keeps one column group");
     constexpr int RS = T / Q;  // rows between a thread's rows
     constexpr int FIT = CAP / 4 / LDN;
-    // Rows per pass: whole 32-row blocks that fit in LDS, and at most 8 rows
-    // per thread with two waves per SIMD (12 with one), which bounds the
-    // registers holding the pass's residual next to the accumulators.
-    constexpr int PR0 = FIT >= BM ? BM : (FIT / 32) * 32;
-    constexpr int PRC = ((T >= 512 ? 8 : 12) * RS) / 32 * 32;
-    constexpr int PR = PR0 < PRC ? PR0 : (PRC >= 32 ? PRC : 32);
-    static_assert(PR >= 32 && PR <= PR0, "LDS too small to stage 32 rows of the tile");
-    constexpr int RU = (PR + RS - 1) / RS;
+    // Rows per pass: whole 32-row blocks that fit in LDS (PRN). When a
+    // residual or per-row bias is read, at most RU = 8 rows per thread (PRL),
+    // which bounds the registers holding the pass's requested rows; the rows
+    // of a pass are then handled in chunks of RU rows per thread.
+    constexpr int PRN = FIT >= BM ? BM : (FIT / 32) * 32;
+    static_assert(PRN >= 32, "LDS too small to stage 32 rows of the tile");
+    constexpr int RU = 8;
+    constexpr int PRC = (RU * RS) / 32 * 32;
+    constexpr int PRL = PRN < PRC ? PRN : (PRC >= 32 ? PRC : 32);
+    static_assert(PRL <= RU * RS || RS > RU * RS, "a loading pass fits one chunk of rows");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     EpiRows e;
@@ -608,43 +613,49 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
     e.rvec = e.ncols == 4 && e.use_r && g.srn == 1 && g.srm % 4 == 0 &&
              ((uintptr_t)g.R + (uintptr_t)((e.r_off + e.gn0) * r_es)) % (uintptr_t)(4 * r_es) == 0;
     e.rmode = (!e.rvec || r_es == 4) ? 0 : (g.r_dtype == DG_BF16 ? 1 : 2);
-    uint32_t raw[RU][4];
-    float br[RU];
+    // One pass loop per pass size (compile-time, so the staging of each
+    // fragment block resolves statically): PRL when rows are requested ahead.
+    auto passes = [&](auto pr_tag) {
+        constexpr int PR = decltype(pr_tag)::value;
+        constexpr bool LOADS = PR == PRL && PRL != PRN;
+        uint32_t raw[RU][2];
+        float br[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u) raw[u][0] = raw[u][1] = 0u, br[u] = 0.0f;
 #pragma unroll 1
-    for (int p0 = 0; p0 < BM; p0 += PR) {
-        e.m_row0 = m0 + p0;
-        e.rows = min(PR, g.M - m0 - p0);
-        epi_load<RU>(g, e, raw, br);
-        __syncthreads();  // the previous pass (or the K loop) is done with the LDS
+        for (int p0 = 0; p0 < BM; p0 += PR) {
+            e.m_row0 = m0 + p0;
+            e.rows = min(PR, g.M - m0 - p0);
+            if (LOADS || PRL == PRN) epi_load<RU>(g, e, raw, br);
+            __syncthreads();  // the previous pass (or the K loop) is done with the LDS
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int rb = wm * WTM + i * 32 - p0;  // block's first row within this pass
-            if (rb < 0 || rb >= PR) continue;
+            for (int i = 0; i < FM; ++i) {
+                const int rb = wm * WTM + i * 32 - p0;  // block's first row within this pass
+                if (rb < 0 || rb >= PR) continue;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = wn * WTN + j * 32 + (lane & 31);
+                for (int j = 0; j < FN; ++j) {
+                    const int col = wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    st[(rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDN + col] = acc[i][j][r];
+                    for (int r = 0; r < 16; ++r)
+                        st[(rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LDN + col] = acc[i][j][r];
+                }
+            }
+            __syncthreads();
+            if (e.ncols <= 0) continue;
+            // The pass in chunks of RU rows per thread (one chunk when rows
+            // were requested ahead: PRL <= RU * RS).
+#pragma unroll 1
+            for (int c = 0; c < PR; c += RU * RS) {
+                EpiRows ec = e;
+                ec.r0 = e.r0 + c;
+                if (g.act == DG_ACT_GELU) epi_rows<DG_ACT_GELU, RU>(g, ec, raw, br);
+                else if (g.act == DG_ACT_RELU) epi_rows<DG_ACT_RELU, RU>(g, ec, raw, br);
+                else epi_rows<DG_ACT_NONE, RU>(g, ec, raw, br);
             }
         }
-        __syncthreads();
-        if (e.ncols <= 0) continue;
-        const int out = g.out_dtype;
-        if (g.act == DG_ACT_GELU) {
-            if (out == DG_BF16) epi_rows<DG_ACT_GELU, DG_BF16, RU>(g, e, raw, br);
-            else if (out == DG_F16) epi_rows<DG_ACT_GELU, DG_F16, RU>(g, e, raw, br);
-            else epi_rows<DG_ACT_GELU, DG_F32, RU>(g, e, raw, br);
-        } else if (g.act == DG_ACT_RELU) {
-            if (out == DG_BF16) epi_rows<DG_ACT_RELU, DG_BF16, RU>(g, e, raw, br);
-            else if (out == DG_F16) epi_rows<DG_ACT_RELU, DG_F16, RU>(g, e, raw, br);
-            else epi_rows<DG_ACT_RELU, DG_F32, RU>(g, e, raw, br);
-        } else {
-            if (out == DG_BF16) epi_rows<DG_ACT_NONE, DG_BF16, RU>(g, e, raw, br);
-            else if (out == DG_F16) epi_rows<DG_ACT_NONE, DG_F16, RU>(g, e, raw, br);
-            else epi_rows<DG_ACT_NONE, DG_F32, RU>(g, e, raw, br);
-        }
-    }
+    };
+    if (PRL == PRN || e.use_r || e.row_bias) passes(std::integral_constant<int, PRL>{});
+    else passes(std::integral_constant<int, PRN>{});
 }
 
 // ---- split-K -------------------------------------------------------------------
