@@ -101,6 +101,24 @@ __device__ __forceinline__ float normal_tail(float x) {
     return e * t * p;
 }
 
+// The same tail for results that are rounded to a 16-bit type: P of degree
+// 6 (3.8e-6 relative error on [0, 14], fit_normal_tail.py --degree 6) and a
+// plain fp32 exponent (relative error about 5e-8 * x^2). Below 1.5e-5
+// relative wherever Q is an fp32 normal, which is under 1/16 of half an ulp
+// of fp16 and 1/130 of bf16's: at most a rare last-bit difference after
+// rounding, for a third fewer operations.
+__device__ __forceinline__ float normal_tail_16(float x) {
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3f * x);
+    float p = -0.0124396523f;
+    p = __builtin_fmaf(p, t, -0.0353136659f);
+    p = __builtin_fmaf(p, t, 0.160478696f);
+    p = __builtin_fmaf(p, t, 0.0202635769f);
+    p = __builtin_fmaf(p, t, 0.131027669f);
+    p = __builtin_fmaf(p, t, 0.116067156f);
+    p = __builtin_fmaf(p, t, 0.119914405f);
+    return __builtin_amdgcn_exp2f(x * x * -0.72134752044448170368f) * t * p;
+}
+
 // ReLU keeps NaN and -0 (only v < 0 becomes +0). GELU is v * Phi(v), with
 // Phi(v) = 1 - Q(v) for v >= 0 and Q(-v) below: no cancellation for large
 // negative v. |v| is clamped at 30, where Q is exactly 0 in fp32, so
@@ -112,6 +130,14 @@ __device__ __forceinline__ float activate(float v, int act) {
         return v * (v >= 0.0f ? 1.0f - q : q);
     }
     return v;
+}
+
+// GELU for a result that is rounded to bf16 or fp16 next (the fused
+// epilogue's 16-bit outputs); an internal activation code, not in the ABI.
+constexpr int kActGelu16 = 100;
+__device__ __forceinline__ float gelu_16(float v) {
+    const float q = normal_tail_16(fminf(fabsf(v), 30.0f));
+    return v * (v >= 0.0f ? 1.0f - q : q);
 }
 
 // C[gm, gn] = act(alpha * v + beta * R[gm, gn] + bias) for one element.
@@ -549,6 +575,7 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, co
             float t = __builtin_fmaf(g.beta, rv[k], g.alpha * x[k]) + (e.bcol[k] + br[u]);
             if constexpr (ACT == DG_ACT_RELU) t = t < 0.0f ? 0.0f : t;
             if constexpr (ACT == DG_ACT_GELU) t = activate(t, DG_ACT_GELU);
+            if constexpr (ACT == kActGelu16) t = gelu_16(t);
             y[k] = t;
         }
         char *cp = e.C + ((int64_t)(e.m_row0 + row) * g.scm + (int64_t)e.gn0 * g.scn) * e.c_es;
@@ -648,7 +675,8 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
             for (int c = 0; c < PR; c += RU * RS) {
                 EpiRows ec = e;
                 ec.r0 = e.r0 + c;
-                if (g.act == DG_ACT_GELU) epi_rows<DG_ACT_GELU, RU>(g, ec, raw, br);
+                if (g.act == DG_ACT_GELU && g.out_dtype == DG_F32) epi_rows<DG_ACT_GELU, RU>(g, ec, raw, br);
+                else if (g.act == DG_ACT_GELU) epi_rows<kActGelu16, RU>(g, ec, raw, br);
                 else if (g.act == DG_ACT_RELU) epi_rows<DG_ACT_RELU, RU>(g, ec, raw, br);
                 else epi_rows<DG_ACT_NONE, RU>(g, ec, raw, br);
             }

@@ -2,8 +2,9 @@
 
 Q(x) = Phi(-x) = erfc(x / sqrt 2) / 2 for x >= 0 is written as
     Q(x) = exp(-x^2 / 2) * t * P(t),   t = 1 / (1 + 0.3 x),
-with P a degree-9 polynomial. The exp factor carries the Gaussian decay, so
-P varies slowly on t in (0, 1] and a low degree fits it to ~3.5e-9 relative
+with P a degree-9 polynomial (degree 6 for results rounded to 16 bits). The
+exp factor carries the Gaussian decay, so P varies slowly on t in (0, 1] and
+a low degree fits it to ~3.5e-9 (degree 9) or ~3.8e-6 (degree 6) relative
 error over x in [0, 14] (beyond, Q is below fp32's normal range). Coefficients
 come from least squares on the relative error, reweighted toward minimax;
 the reference values are computed to 40 digits with mpmath. Run it to
@@ -32,6 +33,10 @@ def fit():
 
 
 if __name__ == "__main__":
+    import sys
+    # --degree N: the degree of P (9 for the fp32 tail, 6 for the 16-bit one)
+    if "--degree" in sys.argv:
+        DEG = int(sys.argv[sys.argv.index("--degree") + 1])
     c, err = fit()
     print(f"max relative fit error {err:.3e}")
     print(", ".join(f"{float(np.float32(v)):.9g}f" for v in c))

@@ -20,7 +20,7 @@ import torch
 import dense_gemm_07_amd as dg
 import oracle
 from dense_gemm_07_amd import inputs
-from helpers import (assert_bits_equal, assert_within_tol, epilogue_tolerance, out_bits, to_f64)
+from helpers import (assert_bits_equal, assert_within_tol, epilogue_tolerance, out_bits, to_f64, ulp)
 
 pytestmark = pytest.mark.gpu
 
@@ -279,6 +279,28 @@ def test_epilogue_random(act, in_dtype, out_dtype):
     case = (in_dtype, out_dtype, 1.5, -0.75, "bf16col", "f32col", act)
     check_epilogue(257, 190, 333, case, ("row", "row"), integers=False, seed=7)
     check_epilogue(64, 64, 4096, case, ("mis", "col"), integers=False, seed=8)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_gelu_alone_accuracy(out_dtype):
+    """The epilogue's GELU by itself: C = GELU(x * 1) with K = 1, so the
+    product is exact, over x in [-14, 14] (every bf16 value there that the
+    grid hits). fp32 C uses the degree-9 tail: within 2^-19 relative of the
+    oracle's erfc form (the device claims 7 ulp). 16-bit C uses the degree-6
+    tail: within 1.5e-5 relative before the rounding, plus half an ulp."""
+    xs = torch.linspace(-14.0, 14.0, 8001).to(torch.bfloat16).unique()
+    M, N = xs.numel(), 64
+    a = xs.reshape(M, 1)
+    b = torch.ones(1, N, dtype=torch.bfloat16)
+    note(f"gelu alone -> {out_dtype}")
+    c = dg.gemm_ex(a.to(DEV), b.to(DEV), out_dtype=TD[out_dtype], activation="gelu")
+    torch.cuda.synchronize()
+    ref = oracle.epilogue(ref_product(a, b, "bf16"), act="gelu")
+    got = to_f64(c)
+    mag = np.maximum(np.abs(got), np.abs(ref))
+    rel = 2.0 ** -19 if out_dtype == "f32" else 1.5e-5
+    tol = rel * mag + 2.0 ** -40 + (0.5 * ulp(out_dtype, mag) if out_dtype != "f32" else 0.0)
+    assert_within_tol(got, ref, tol, f"gelu alone -> {out_dtype}")
 
 
 def test_epilogue_beta_zero_never_reads_c():
