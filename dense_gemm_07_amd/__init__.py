@@ -289,11 +289,12 @@ DEFAULT_WORKSPACE_BYTES = 64 << 20
 _workspaces = {}
 
 
-def _workspace(device, nbytes):
-    import torch
-    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+def _workspace(t, nbytes):
+    """The cached split-K workspace of tensor t's GPU (grown to nbytes if needed)."""
+    key = t.get_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        import torch
         ws = torch.empty(max(nbytes, DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=f"cuda:{key}")
         _workspaces[key] = ws
     return ws
@@ -332,7 +333,7 @@ def _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation):
     if cshape != (M, N):
         raise ValueError(f"out must be {(M, N)} per product, got {cshape}")
     for name, t in (("A", a), ("B", b), ("out", out), ("residual", residual), ("bias", bias)):
-        if t is not None and t.device.type != "cuda":
+        if t is not None and not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
     if activation not in ACTIVATIONS:
         raise ValueError(f"activation must be one of {sorted(k for k in ACTIVATIONS if k)}")
@@ -394,7 +395,7 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
         need = 0
         if config is not None and config.k_splits > 1:
             need = workspace_size(prob[0], prob[1], prob[2], batch.count, config)
-        ws = _workspace(a.device, need)
+        ws = _workspace(a, need)
         ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     elif workspace is not None and workspace is not False:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -410,7 +411,7 @@ def autotune_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual
     prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
     ws_ptr, ws_bytes = None, 0
     if workspace is True:
-        ws = _workspace(a.device, 0)
+        ws = _workspace(a, 0)
         ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     elif workspace is not None and workspace is not False:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -509,7 +510,7 @@ def attention(q, k, v, out=None, out_dtype=None, scale=None, causal=False, retur
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.device.type != "cuda":
+        if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
         if D > 1 and t.stride(3) != 1:
             raise ValueError(f"{name} needs a unit stride along head_dim")
