@@ -187,6 +187,9 @@ def main():
                     help="time an explicit kernel config BMxBNxBK:waves:stages:group_m:xcd_remap (ablations)")
     ap.add_argument("--misalign-a", action="store_true",
                     help="view A one element past a 16-byte boundary (forces the register-staged kernel)")
+    ap.add_argument("--rotate", type=int, default=1, metavar="SETS",
+                    help="cycle the plain product through SETS copies of (A, B, C), so that more than the "
+                         "256 MB Infinity Cache is touched between reuses (cold-cache numbers)")
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch.matmul (the ROCm vendor GEMM) on the same operands, for context")
     ap.add_argument("--attention", action="store_true",
@@ -293,6 +296,14 @@ def main():
     elif ex:
         def step():
             dg.gemm_ex(a, b, out=c, stream=stream, workspace=True if args.split_k else None, config=explicit, **epi)
+    elif args.rotate > 1:
+        sets = [(a, b, c)] + [(a.clone(), b.clone(), torch.empty_like(c)) for _ in range(args.rotate - 1)]
+        turn = [0]
+
+        def step():
+            sa, sb, sc = sets[turn[0]]
+            turn[0] = (turn[0] + 1) % len(sets)
+            dg.gemm(sa, sb, out=sc, stream=stream)
     else:
         def step():
             dg.gemm(a, b, out=c, stream=stream)
@@ -307,6 +318,19 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+
+    # Per-launch durations (median, min, p90) from an event pair around each
+    # launch, in a second pass over the same number of steps, so the events do
+    # not enter the throughput figure above.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    launch_us = {"median": round(per[len(per) // 2], 2), "min": round(per[0], 2),
+                 "p90": round(per[min(len(per) - 1, int(0.9 * len(per)))], 2)}
 
     flops = w.flops * nb
     nbytes = w.compulsory_bytes() * nb + extra_bytes
@@ -339,7 +363,11 @@ def main():
                    "b_layout": "col-major" if w.b_colmajor else "row-major",
                    "kernel_config": cfg.as_dict(), "autotune_s": round(tune_s, 3)},
         "roofline": roofline,
+        "launch_us": launch_us,
     }
+    if args.rotate > 1:
+        result["config"]["rotate_sets"] = args.rotate
+        result["roofline"]["traffic"] = None
     if ex:
         result["config"].update({"epilogue": args.epilogue, "batch": nb, "split_k_allowed": args.split_k})
     if args.config or args.misalign_a:
