@@ -588,11 +588,11 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, co
 // The same tile through the fused epilogue, staged through LDS. The tile is
 // written to LDS (fp32, rows padded by 4 floats) in passes of whole 32-row
 // fragment blocks. Each thread then owns one 4-column group of the tile
-// (T is a multiple of BN/4) and RU rows of each pass: a per-column bias is
-// loaded once per tile, the pass's residual rows are requested before the
-// staging (epi_load), and a row's 4 elements of C and of the residual move as
-// one vector when the layout allows. `st` is the kernel's LDS (CAP bytes,
-// free: the K loop is done).
+// (T is a multiple of BN/4) and walks its rows of each pass, RU at a time: a
+// per-column bias is loaded once per tile, the pass's residual rows are
+// requested before the staging (epi_load), and a row's 4 elements of C and of
+// the residual move as one vector when the layout allows. `st` is the
+// kernel's LDS (CAP bytes, free: the K loop is done).
 template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
 __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
                                           float *st, int m0, int n0) {
@@ -612,7 +612,7 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
     constexpr int RU = 8;
     constexpr int PRC = (RU * RS) / 32 * 32;
     constexpr int PRL = PRN < PRC ? PRN : (PRC >= 32 ? PRC : 32);
-    static_assert(PRL <= RU * RS || RS > RU * RS, "a loading pass fits one chunk of rows");
+    static_assert(PRL <= RU * RS, "a loading pass fits one chunk of rows");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     EpiRows e;

@@ -323,3 +323,35 @@ def test_no_unit_stride_operands(in_dtype):
         c = dg.gemm(a, b, out_dtype=TD[out])
         torch.cuda.synchronize()
         assert_bits_equal(out_bits(c, out), want, f"strided {in_dtype} -> {out}")
+
+
+def test_operands_beyond_31_bit_offsets():
+    """Maximum sizes: a row-major B of 2 GiB (32768 x 32768 bf16), whose byte
+    offsets no longer fit the direct loads' 31 bits, then the same matrix as a
+    2 GiB row-major A with a small B. Sampled output columns / rows against
+    the oracle, bit-exact on integer data (|C| <= 2 * 2 * K < 2^24)."""
+    K = 32768
+    g = torch.Generator().manual_seed(71)
+    # B[k, j] = ((7k + 13j) mod 5) - 2, written on the device in row chunks.
+    big = torch.empty((K, K), dtype=torch.bfloat16, device=DEV)
+    cols = torch.arange(K, device=DEV, dtype=torch.int64)
+    for k0 in range(0, K, 1024):
+        ks = torch.arange(k0, k0 + 1024, device=DEV, dtype=torch.int64)[:, None]
+        big[k0:k0 + 1024] = ((7 * ks + 13 * cols[None, :]) % 5 - 2).to(torch.bfloat16)
+    small = torch.randint(-2, 3, (64, K), generator=g).to(torch.bfloat16)
+    pick = [0, 1, 4095, 4096, 12345, 32766, 32767]
+
+    note("A[64, 32768] @ B[32768, 32768] (B 2 GiB)")
+    c = dg.gemm(small.to(DEV), big, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    b_cols = big[:, pick].cpu()
+    want = oracle.encode(ref_full(small, b_cols, "bf16"), "f32")
+    assert_bits_equal(out_bits(c[:, pick].contiguous(), "f32"), want, "2 GiB B, sampled columns")
+
+    note("A[32768, 32768] @ B[32768, 64] (A 2 GiB)")
+    c2 = dg.gemm(big, small.t().contiguous().to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a_rows = big[pick, :].cpu()
+    want2 = oracle.encode(ref_full(a_rows, small.t().contiguous(), "bf16"), "f32")
+    assert_bits_equal(out_bits(c2[pick, :].contiguous(), "f32"), want2, "2 GiB A, sampled rows")
+    del big
