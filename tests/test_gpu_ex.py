@@ -106,6 +106,28 @@ def test_split_k_integers_bit_exact(shape, splits):
                 assert_bits_equal(out_bits(c, out_dtype), want, what)
 
 
+def test_split_k_longest_k():
+    """K = 2^20 with a 64 x 64 output: one tile, so the library's split (with a
+    workspace) is the largest it makes (16 ranges of 65536), and the unsplit
+    loop runs 16384 K steps. Sampled columns, bit-exact on integers
+    (|C| <= 4K = 2^22 < 2^24)."""
+    M, N, K = 64, 64, 1 << 20
+    g = torch.Generator().manual_seed(91)
+    a = torch.randint(-2, 3, (M, K), generator=g).to(torch.bfloat16)
+    b = torch.randint(-2, 3, (K, N), generator=g).to(torch.bfloat16)
+    cols = [0, 17, 63]
+    want = oracle.encode(ref_product(a, b[:, cols].contiguous(), "bf16"), "f32")
+    ad, bd = a.to(DEV), b.to(DEV)
+    cfg, _ = dg.select_config_ex(M, N, K, ad.stride(), bd.stride(), (N, 1), CODE["bf16"], CODE["f32"],
+                                 workspace_bytes=dg.DEFAULT_WORKSPACE_BYTES)
+    assert cfg.k_splits == 16, cfg.k_splits
+    for ws in (True, None):
+        note(f"K = 2^20, workspace={ws}")
+        c = dg.gemm_ex(ad, bd, out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert_bits_equal(out_bits(c[:, cols].contiguous(), "f32"), want, f"K=2^20 workspace={ws}")
+
+
 @pytest.mark.parametrize("in_dtype,out_dtype", [("f16", "f16"), ("bf16", "f32"), ("bf16", "bf16")])
 def test_split_k_random_within_tolerance(in_dtype, out_dtype):
     for (M, N, K), splits in [((300, 200, 3000), 4), ((96, 1000, 5000), 7), ((1, 700, 4100), 16)]:
