@@ -203,3 +203,26 @@ def test_attention_rejects_unsupported():
     mis = buf[1:].view(1, 1, 8, 64)
     with pytest.raises(dg.DGError):
         dg.attention(mis, mis, mis)  # not 16-byte aligned
+
+
+def test_attention_long_sequence_sampled():
+    """seq 32768 at head_dim 128 (the K/V ring walks 512 key blocks), causal
+    and not, sampled query rows against the oracle on their allowed keys."""
+    B, H, S, D = 1, 2, 32768, 128
+    q, k, v = (draw((B, H, S, D), "bf16", s) for s in (41, 42, 43))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    rows = [0, 1, 127, 128, 16383, 32767]
+    vmax = np.abs(v.double().numpy()).max(axis=2, keepdims=True)
+    for causal in (False, True):
+        note(f"seq 32768 causal={causal}")
+        o, lse = dg.attention(qd, kd, vd, causal=causal, return_lse=True)
+        torch.cuda.synchronize()
+        for i in rows:
+            n = i + 1 if causal else S
+            ref, ref_lse = oracle.attention(inputs.bits(q[:, :, i:i + 1], "bf16"), inputs.bits(k[:, :, :n], "bf16"),
+                                            inputs.bits(v[:, :, :n], "bf16"), "bf16")
+            got = o[:, :, i:i + 1].double().cpu().numpy()
+            tol = 2 * U_IN["bf16"] * vmax + 1e-5 * (1 + vmax) + 0.5 * ulp("bf16", np.maximum(np.abs(got), np.abs(ref)))
+            assert np.all(np.abs(got - ref) <= tol), f"row {i} causal={causal} max err {np.abs(got - ref).max()}"
+            gl = lse[:, :, i:i + 1].double().cpu().numpy()
+            assert np.all(np.abs(gl - ref_lse) <= 1e-4 * (1 + np.abs(ref_lse))), f"lse row {i} causal={causal}"
