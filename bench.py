@@ -296,7 +296,7 @@ def main():
     elif ex:
         def step():
             dg.gemm_ex(a, b, out=c, stream=stream, workspace=True if args.split_k else None, config=explicit, **epi)
-    elif args.rotate > 1:
+    elif args.rotate > 1:  # plain product only
         sets = [(a, b, c)] + [(a.clone(), b.clone(), torch.empty_like(c)) for _ in range(args.rotate - 1)]
         turn = [0]
 
@@ -365,7 +365,7 @@ def main():
         "roofline": roofline,
         "launch_us": launch_us,
     }
-    if args.rotate > 1:
+    if args.rotate > 1 and explicit is None and not ex:  # the plain product is the one rotated
         result["config"]["rotate_sets"] = args.rotate
         result["roofline"]["traffic"] = None
     if ex:
