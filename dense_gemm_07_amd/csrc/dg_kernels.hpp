@@ -306,12 +306,34 @@ struct TileLoader {
     static constexpr int NREG = MODE == LD_RU ? PERB * 8 : PER;
 
     u32x4 reg[NREG];
+    bool okc[PER];         // LD_KU: chunk c is inside the operand (else LDS gets zeros)
     const uint16_t *base;  // element (row0, k = 0) of the operand
     int64_t srow, sk;      // element strides along rows and along k
     int rows_valid;        // rows of the tile inside the operand
     int K;
 
+    // INSIDE_K: the caller knows k0 + BK <= K. Then the LD_KU chunks are one
+    // 16-byte load each, from a row clamped into the operand, with no branch:
+    // a branch around the load (the element loads at the K tail) makes the
+    // compiler wait for the load where the two paths join, i.e. at once. The
+    // row mask is applied when the chunk is written to LDS (store).
+    template <bool INSIDE_K = false>
     __device__ __forceinline__ void load(int tid, int k0) {
+        if constexpr (MODE == LD_KU && INSIDE_K) {
+#pragma unroll
+            for (int c = 0; c < PER; ++c) {
+                const int q = c * T + tid;
+                const int r = q / KCH, kc = q % KCH;
+                okc[c] = ((NCH % T == 0) || q < NCH) && r < rows_valid;
+                const int rr = r < rows_valid ? r : (rows_valid > 0 ? rows_valid - 1 : 0);
+                reg[c] = load16_unaligned(base + (int64_t)rr * srow + k0 + kc * 8);
+            }
+            return;
+        }
+        if constexpr (MODE == LD_KU) {
+#pragma unroll
+            for (int c = 0; c < PER; ++c) okc[c] = true;
+        }
         if constexpr (MODE == LD_RU) {
 #pragma unroll
             for (int b = 0; b < PERB; ++b) {
@@ -392,7 +414,9 @@ struct TileLoader {
                 const int q = c * T + tid;
                 if ((NCH % T == 0) || q < NCH) {
                     const int r = q / KCH, kc = q % KCH;
-                    *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = reg[c];
+                    u32x4 v = reg[c];
+                    if constexpr (MODE == LD_KU) v = okc[c] ? v : u32x4{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = v;
                 }
             }
         }
@@ -776,20 +800,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    TileLoader<BM, BK, LDK, T, LA> la;
-    TileLoader<BN, BK, LDK, T, LB> lb;
+    // P register sets for the global loads: slice kt+P-1 is requested at
+    // step kt and written to LDS at step kt+P-2, so P-1 steps of products
+    // cover a load's latency. Small tiles do little work per step and take
+    // 4 sets; 128x128 and larger keep 2 (their registers are the limit).
+    constexpr int P = BM * BN < 128 * 128 ? 4 : 2;
+    // With P = 2 one set serves both roles (requested at the top of a step,
+    // written at its end), as the register budget of the large tiles needs.
+    constexpr int NSET = P == 2 ? 1 : P;
+    TileLoader<BM, BK, LDK, T, LA> la[NSET];
+    TileLoader<BN, BK, LDK, T, LB> lb[NSET];
     const uint16_t *A = static_cast<const uint16_t *>(g.A) + (int64_t)w.prod * g.bsa;
     const uint16_t *B = static_cast<const uint16_t *>(g.B) + (int64_t)w.prod * g.bsb;
-    la.base = A + (int64_t)m0 * g.sam + (int64_t)k_begin * g.sak;
-    la.srow = g.sam;
-    la.sk = g.sak;
-    la.rows_valid = min(BM, g.M - m0);
-    la.K = kl;
-    lb.base = B + (int64_t)n0 * g.sbn + (int64_t)k_begin * g.sbk;
-    lb.srow = g.sbn;
-    lb.sk = g.sbk;
-    lb.rows_valid = min(BN, g.N - n0);
-    lb.K = kl;
+#pragma unroll
+    for (int p = 0; p < NSET; ++p) {
+        la[p].base = A + (int64_t)m0 * g.sam + (int64_t)k_begin * g.sak;
+        la[p].srow = g.sam;
+        la[p].sk = g.sak;
+        la[p].rows_valid = min(BM, g.M - m0);
+        la[p].K = kl;
+        lb[p].base = B + (int64_t)n0 * g.sbn + (int64_t)k_begin * g.sbk;
+        lb[p].srow = g.sbn;
+        lb[p].sk = g.sbk;
+        lb[p].rows_valid = min(BN, g.N - n0);
+        lb[p].K = kl;
+    }
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -800,11 +835,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = (kl + BK - 1) / BK;
+#pragma unroll
+    for (int p = 0; p + 1 < P; ++p) {
+        if (p < nk) {
+            if (P > 2 && (p + 1) * BK <= kl) {
+                la[p % NSET].template load<true>(tid, p * BK);
+                lb[p % NSET].template load<true>(tid, p * BK);
+            } else {
+                la[p % NSET].load(tid, p * BK);
+                lb[p % NSET].load(tid, p * BK);
+            }
+        }
+    }
     if (nk > 0) {
-        la.load(tid, 0);
-        lb.load(tid, 0);
-        la.store(tid, lds[0]);
-        lb.store(tid, lds[0] + BM * LDK);
+        la[0].store(tid, lds[0]);
+        lb[0].store(tid, lds[0] + BM * LDK);
         __syncthreads();
     }
 
@@ -812,33 +857,86 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
     const int a_row = (wm * WTM + (lane & 31)) * LDK + (lane >> 5) * 8;
     const int b_row = (BM + wn * WTN + (lane & 31)) * LDK + (lane >> 5) * 8;
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(tid, (kt + 1) * BK);
-            lb.load(tid, (kt + 1) * BK);
-        }
-        const uint16_t *s = lds[cur];
+    // Step kt: request slice kt+P-1 into set (kt+P-1) % P, multiply slice kt
+    // (LDS buffer kt & 1), write slice kt+1 from set (kt+1) % P into the other
+    // buffer (read in step kt-1, before the last barrier). Steps run P at a
+    // time so the set and buffer indices are compile-time (P is even).
+    static_assert(P % 2 == 0, "buffer parity follows the step within a group");
+    auto multiply = [&](int u) {
+        const uint16_t *s = lds[u & 1];
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             u32x4 af[FM], bf[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const u32x4 *>(s + a_row + i * 32 * LDK + kk * 16);
+            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(s + a_row + i * 32 * LDK + kk * 16);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const u32x4 *>(s + b_row + j * 32 * LDK + kk * 16);
+            for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(s + b_row + j * 32 * LDK + kk * 16);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<TI>::run(af[i], bf[j], acc[i][j]);
         }
-        if (more) {
-            la.store(tid, lds[cur ^ 1]);
-            lb.store(tid, lds[cur ^ 1] + BM * LDK);
+    };
+    if constexpr (P == 2) {
+        // The large tiles: one register set, requested at the top of a step
+        // and written at its end (their registers do not allow more).
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < nk;
+            if (more) {
+                la[0].load(tid, (kt + 1) * BK);
+                lb[0].load(tid, (kt + 1) * BK);
+            }
+            multiply(cur);
+            if (more) {
+                la[0].store(tid, lds[cur ^ 1]);
+                lb[0].store(tid, lds[cur ^ 1] + BM * LDK);
+            }
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        // Groups whose every step exists and requests a slice wholly inside
+        // K: straight-line code (no branch between a load and the write of
+        // its data), so the compiler waits for each set only when it is
+        // written.
+        const int n_in = kl / BK;  // slices wholly inside K
+        int kt0 = 0;
+        for (; kt0 + 2 * P - 2 < n_in; kt0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) {
+                const int kt = kt0 + u;
+                la[(u + P - 1) % P].template load<true>(tid, (kt + P - 1) * BK);
+                lb[(u + P - 1) % P].template load<true>(tid, (kt + P - 1) * BK);
+                multiply(u);
+                la[(u + 1) % P].store(tid, lds[(u & 1) ^ 1]);
+                lb[(u + 1) % P].store(tid, lds[(u & 1) ^ 1] + BM * LDK);
+                __syncthreads();
+            }
+        }
+        // The remaining steps, each guarded (the K tail and the end).
+        for (; kt0 < nk; kt0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) {
+                const int kt = kt0 + u;
+                if (kt >= nk) break;
+                if (kt + P - 1 < nk) {
+                    const int k0 = (kt + P - 1) * BK;
+                    if (k0 + BK <= kl) {
+                        la[(u + P - 1) % P].template load<true>(tid, k0);
+                        lb[(u + P - 1) % P].template load<true>(tid, k0);
+                    } else {
+                        la[(u + P - 1) % P].load(tid, k0);
+                        lb[(u + P - 1) % P].load(tid, k0);
+                    }
+                }
+                multiply(u);
+                if (kt + 1 < nk) {
+                    la[(u + 1) % P].store(tid, lds[(u & 1) ^ 1]);
+                    lb[(u + 1) % P].store(tid, lds[(u & 1) ^ 1] + BM * LDK);
+                }
+                __syncthreads();
+            }
+        }
     }
 
     // Epilogue: fp32 accumulators -> C's dtype, masked to C's view.
