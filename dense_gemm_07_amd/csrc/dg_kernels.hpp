@@ -312,13 +312,33 @@ struct TileLoader {
     int rows_valid;        // rows of the tile inside the operand
     int K;
 
-    // INSIDE_K: the caller knows k0 + BK <= K. Then the LD_KU chunks are one
-    // 16-byte load each, from a row clamped into the operand, with no branch:
-    // a branch around the load (the element loads at the K tail) makes the
-    // compiler wait for the load where the two paths join, i.e. at once. The
-    // row mask is applied when the chunk is written to LDS (store).
+    // INSIDE_K: the caller knows k0 + BK <= K and, for LD_RU, that every row
+    // of the tile is inside the operand. Then the loads have no branch: a
+    // branch around a load (the element loads at the edges) makes the
+    // compiler wait for the load where the two paths join, i.e. at once.
+    // LD_KU chunks are one 16-byte load each from a row clamped into the
+    // operand; the row mask is applied when the chunk is written to LDS
+    // (store). LD_RU blocks past the tile's block count repeat the last
+    // block's loads (store skips them).
     template <bool INSIDE_K = false>
     __device__ __forceinline__ void load(int tid, int k0) {
+        if constexpr (MODE == LD_RU && INSIDE_K) {
+#pragma unroll
+            for (int b = 0; b < PERB; ++b) {
+                const int q = b * T + tid;
+                const int qc = (NBL % T == 0) ? q : (q < NBL ? q : NBL - 1);
+                const int kb = qc % KCH, r0 = (qc / KCH) * 8;
+                u32x4 raw[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    raw[j] = load16_unaligned(base + (int64_t)(k0 + kb * 8 + j) * sk + r0);
+                u32x4 t[8];
+                transpose8x8(raw, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) reg[b * 8 + i] = t[i];
+            }
+            return;
+        }
         if constexpr (MODE == LD_KU && INSIDE_K) {
 #pragma unroll
             for (int c = 0; c < PER; ++c) {
@@ -835,10 +855,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = (kl + BK - 1) / BK;
+    // Slices [0, n_fast) take the branch-free loads: wholly inside K, and a
+    // row-contiguous operand's tile has all its rows.
+    const bool full_rows = (LA != LD_RU || la[0].rows_valid == BM) && (LB != LD_RU || lb[0].rows_valid == BN);
+    const int n_fast = full_rows ? kl / BK : 0;
 #pragma unroll
     for (int p = 0; p + 1 < P; ++p) {
         if (p < nk) {
-            if (P > 2 && (p + 1) * BK <= kl) {
+            if (full_rows && (p + 1) * BK <= kl) {  // p < n_fast
                 la[p % NSET].template load<true>(tid, p * BK);
                 lb[p % NSET].template load<true>(tid, p * BK);
             } else {
@@ -879,8 +903,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
     };
     if constexpr (P == 2) {
         // The large tiles: one register set, requested at the top of a step
-        // and written at its end (their registers do not allow more).
-        for (int kt = 0; kt < nk; ++kt) {
+        // and written at its end (their registers do not allow more). First
+        // the steps whose next slice takes the branch-free loads, then the
+        // rest, guarded.
+        int kt = 0;
+        // LD_GN has no branch-free load (both operands use it or neither).
+        // At BK 32 the compiler spills this loop heavily with LD_RU, so
+        // those tiles keep the guarded loop.
+        if constexpr (LA != LD_GN && BK >= 64)
+        for (; kt + 2 <= n_fast; ++kt) {
+            la[0].template load<true>(tid, (kt + 1) * BK);
+            lb[0].template load<true>(tid, (kt + 1) * BK);
+            multiply(kt & 1);
+            la[0].store(tid, lds[(kt & 1) ^ 1]);
+            lb[0].store(tid, lds[(kt & 1) ^ 1] + BM * LDK);
+            __syncthreads();
+        }
+        for (; kt < nk; ++kt) {
             const int cur = kt & 1;
             const bool more = kt + 1 < nk;
             if (more) {
@@ -895,13 +934,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
             __syncthreads();
         }
     } else {
-        // Groups whose every step exists and requests a slice wholly inside
-        // K: straight-line code (no branch between a load and the write of
-        // its data), so the compiler waits for each set only when it is
-        // written.
-        const int n_in = kl / BK;  // slices wholly inside K
+        // Groups whose every step exists and requests a slice below n_fast:
+        // straight-line code (no branch between a load and the write of its
+        // data), so the compiler waits for each set only when it is written.
         int kt0 = 0;
-        for (; kt0 + 2 * P - 2 < n_in; kt0 += P) {
+        for (; kt0 + 2 * P - 2 < n_fast; kt0 += P) {
 #pragma unroll
             for (int u = 0; u < P; ++u) {
                 const int kt = kt0 + u;
@@ -921,7 +958,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
                 if (kt >= nk) break;
                 if (kt + P - 1 < nk) {
                     const int k0 = (kt + P - 1) * BK;
-                    if (k0 + BK <= kl) {
+                    if (full_rows && k0 + BK <= kl) {  // slice below n_fast
                         la[(u + P - 1) % P].template load<true>(tid, k0);
                         lb[(u + P - 1) % P].template load<true>(tid, k0);
                     } else {
