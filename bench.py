@@ -19,6 +19,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense: MFMA bf16/fp16, fp32
+SPEC_SCLK_MHZ = 2400.0  # the shader clock the peaks above assume
 HBM_GBPS = 8000.0
 METRIC = "TFLOP/s and % of MFMA dense peak, 4096³ bf16 GEMM on 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
@@ -118,6 +119,100 @@ def cpu_baseline(w, a_cpu, b_cpu, target_s=10.0):
                       f"{dt:.2f} s wall, fp64 k-ascending sums"}
 
 
+def warm_up(step, steps, settle_ms):
+    """The untimed warm-up: `steps` steps, then more until `settle_ms` of wall time has passed since
+    the first. When a load starts from idle, the board's power manager first lets the clock run high,
+    then pulls it down past its sustained level for some 10 ms before settling (a kernel trace of
+    back-to-back 4096^3 launches: 107 us, then 116-140 us, then a steady 105.7 us). A timed region
+    inside that dip measures the transient, not the sustained rate. Returns the extra steps run."""
+    import torch
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    extra, batch = 0, 4
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(batch):
+            step()
+        torch.cuda.synchronize()
+        extra += batch
+        batch = min(2 * batch, 256)
+    return extra
+
+
+def sclk_file(dev_index):
+    """The device's sysfs list of shader clock levels (the current one marked '*'), or None if unreadable."""
+    import torch
+    p = torch.cuda.get_device_properties(dev_index)
+    try:
+        bdf = "%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+    except AttributeError:
+        return None
+    path = f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk"
+    return path if os.access(path, os.R_OK) else None
+
+
+def read_sclk_mhz(path):
+    """The shader clock (MHz) on the marked line of pp_dpm_sclk, or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if line.endswith("*"):
+                    return float(line.split(":", 1)[1].rstrip("*").strip().lower().removesuffix("mhz"))
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def clock_window(step, dev_index, seconds, achieved=None, peak=None):
+    """Shader clock while `step` runs back to back for about `seconds` (after the timed region, so the
+    throughput figure is unaffected). A thread reads pp_dpm_sclk every 5 ms; the steps are issued in
+    batches with a synchronisation between them. With `achieved` and `peak` (a peak quoted at
+    SPEC_SCLK_MHZ) it also gives the peak scaled to the median clock and achieved / that."""
+    import threading
+
+    import torch
+    path = sclk_file(dev_index)
+    if path is None or seconds <= 0:
+        return None
+    before = read_sclk_mhz(path)
+    samples, running = [], threading.Event()
+    running.set()
+
+    def poll():
+        while running.is_set():
+            v = read_sclk_mhz(path)
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.005)
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    batch = 8
+    while time.perf_counter() - t0 < seconds:
+        tb = time.perf_counter()
+        for _ in range(batch):
+            step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - tb < 0.02:
+            batch *= 2
+    running.clear()
+    th.join()
+    after = read_sclk_mhz(path)
+    if not samples:
+        return None
+    ss = sorted(samples)
+    out = {"source": "pp_dpm_sclk", "before_mhz": before, "after_mhz": after,
+           "during_mhz": {"median": ss[len(ss) // 2], "min": ss[0], "max": ss[-1], "samples": len(ss)},
+           "window_s": round(time.perf_counter() - t0, 2), "spec_mhz": SPEC_SCLK_MHZ}
+    if achieved is not None and peak is not None:
+        adj = peak * ss[len(ss) // 2] / SPEC_SCLK_MHZ
+        out["clock_adjusted_peak"] = round(adj, 1)
+        out["frac_of_clock_adjusted_peak"] = round(achieved / adj, 4)
+    return out
+
+
 def bench_attention(args):
     """Attention forward: O = softmax(QK^T/sqrt(d) [causal]) V, [batch, heads, seq, head_dim] bf16."""
     import torch
@@ -132,9 +227,7 @@ def bench_attention(args):
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
     step = lambda: dg.attention(q, k, v, out=o, causal=args.causal, stream=stream)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    settle_steps = warm_up(step, args.warmup, args.settle_ms)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
@@ -157,7 +250,9 @@ def bench_attention(args):
                    "batch": B, "heads": H, "seq": S, "head_dim": D, "causal": args.causal},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None},
+        "settle": {"ms": args.settle_ms, "extra_warmup_steps": settle_steps},
     }
+    result["sclk"] = clock_window(step, dev.index or 0, args.clock_seconds, tflops, peak)
     print(json.dumps(result), flush=True)
 
 
@@ -194,6 +289,12 @@ def main():
                     help="also time torch.matmul (the ROCm vendor GEMM) on the same operands, for context")
     ap.add_argument("--attention", action="store_true",
                     help="time the attention forward kernel instead (--batch, --heads, --seq, --head-dim, --causal)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="keep warming up (beyond --warmup steps) until this much wall time has passed, "
+                         "so the timed steps run at the board's settled clock (0: exactly --warmup steps)")
+    ap.add_argument("--clock-seconds", type=float, default=0.5,
+                    help="after the timed steps, run the same step this long while sampling the shader "
+                         "clock (0: skip)")
     ap.add_argument("--heads", type=int, default=16)
     ap.add_argument("--seq", type=int, default=8192)
     ap.add_argument("--head-dim", type=int, default=64)
@@ -203,8 +304,8 @@ def main():
         record_traffic(args.workload, *args.record_traffic, args.copy_mib, args.commands)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the product shards without exchange, but no multi-GPU path is built).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (a product shards "
+              f"across GPUs without exchange, but the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -307,9 +408,7 @@ def main():
     else:
         def step():
             dg.gemm(a, b, out=c, stream=stream)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    settle_steps = warm_up(step, args.warmup, args.settle_ms)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -364,6 +463,7 @@ def main():
                    "kernel_config": cfg.as_dict(), "autotune_s": round(tune_s, 3)},
         "roofline": roofline,
         "launch_us": launch_us,
+        "settle": {"ms": args.settle_ms, "extra_warmup_steps": settle_steps},
     }
     if args.rotate > 1 and explicit is None and not ex:  # the plain product is the one rotated
         result["config"]["rotate_sets"] = args.rotate
@@ -380,9 +480,7 @@ def main():
 
         def vstep():
             torch.matmul(a, b, out=vout)
-        for _ in range(args.warmup):
-            vstep()
-        torch.cuda.synchronize()
+        warm_up(vstep, args.warmup, args.settle_ms)
         start.record(stream)
         for _ in range(args.steps):
             vstep()
@@ -392,6 +490,11 @@ def main():
         result["vendor"] = {"library": "torch.matmul (hipBLASLt)", "value": round(flops / (vms * 1e-3) / 1e12, 2),
                             "unit": "TFLOP/s", "ms_per_step": round(vms, 5), "speedup_of_ours": round(vms / ms, 4),
                             "out_dtype": str(vout.dtype).replace("torch.", "")}
+    # Observed shader clock (the board lowers it under its power cap); the clock-adjusted
+    # fraction applies to the matrix-core roof only.
+    mfma = roofline["bound"] == "mfma"
+    result["sclk"] = clock_window(step, dev.index or 0, args.clock_seconds,
+                                  tflops if mfma else None, peak if mfma else None)
     if not args.no_cpu_baseline and not ex and not args.config and not args.misalign_a:
         result["cpu_baseline"] = cpu_baseline(w, a_cpu, b_cpu)
     print(json.dumps(result), flush=True)

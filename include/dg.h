@@ -58,7 +58,7 @@ typedef enum dg_dtype {
 typedef enum dg_status {
     DG_OK = 0,
     DG_ERR_INVALID_VALUE = 1,  /* bad dimension, pointer, stride, alignment or dtype */
-    DG_ERR_UNSUPPORTED = 2,    /* valid request this build has no kernel for */
+    DG_ERR_UNSUPPORTED = 2,    /* valid request the library has no kernel for */
     DG_ERR_NO_CONFIG = 3,      /* explicit config invalid for this problem/dtype */
     DG_ERR_HIP = 4             /* a HIP runtime call failed */
 } dg_status;
