@@ -1364,12 +1364,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
 // One workgroup per (product, tile), the thread layout of the MFMA kernel that
 // wrote the partials (WM x WN waves): thread t sums its float4s over the
 // ranges in order 0..S-1 and holds the result in the accumulator layout, so
-// the epilogue is the MFMA kernels' own write_tile.
+// the epilogue is the MFMA kernels' own write_tile. The loads of C ranges
+// are issued together before any of their sums (a thread of a small tile
+// holds only a few float4s, and one range at a time would cost one memory
+// round trip per range); ranges past S-1 in the last group re-read range S-1
+// and are not added.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_split_reduce(GemmArgs g) {
     constexpr int T = WM * WN * 64;
     constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
     constexpr int V = FM * FN * 4;
+    constexpr int C = V >= 16 ? 1 : 16 / V;  // ranges in flight together
     constexpr int CAP = 64 * 1024;  // epilogue staging: at least 32 rows of every tile width
     __shared__ __attribute__((aligned(16))) float st[CAP / 4];
 
@@ -1382,6 +1387,43 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_split_reduce(GemmArgs g) {
     w.pm = t / g.grid_n;
     w.pn = t - w.pm * g.grid_n;
     const float4 *slot = reinterpret_cast<const float4 *>(g.ws) + (int64_t)w.slot * g.splits * (V * T);
+    float4 sum[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) sum[v] = slot[v * T + threadIdx.x];
+    if constexpr (C == 1) {
+        // Enough float4s per thread to keep the memory busy range by range.
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            for (int s = 1; s < g.splits; ++s) {
+                const float4 p = slot[((int64_t)s * V + v) * T + threadIdx.x];
+                sum[v].x += p.x;
+                sum[v].y += p.y;
+                sum[v].z += p.z;
+                sum[v].w += p.w;
+            }
+    } else {
+        for (int s0 = 1; s0 < g.splits; s0 += C) {
+            float4 p[C][V];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int s = min(s0 + c, g.splits - 1);
+#pragma unroll
+                for (int v = 0; v < V; ++v) p[c][v] = slot[((int64_t)s * V + v) * T + threadIdx.x];
+            }
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (s0 + c < g.splits) {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        sum[v].x += p[c][v].x;
+                        sum[v].y += p[c][v].y;
+                        sum[v].z += p[c][v].z;
+                        sum[v].w += p[c][v].w;
+                    }
+                }
+            }
+        }
+    }
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -1389,19 +1431,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_split_reduce(GemmArgs g) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int v = (i * FN + j) * 4 + q;
-                float4 sum = slot[v * T + threadIdx.x];
-                for (int s = 1; s < g.splits; ++s) {
-                    const float4 p = slot[((int64_t)s * V + v) * T + threadIdx.x];
-                    sum.x += p.x;
-                    sum.y += p.y;
-                    sum.z += p.z;
-                    sum.w += p.w;
-                }
-                acc[i][j][4 * q] = sum.x;
-                acc[i][j][4 * q + 1] = sum.y;
-                acc[i][j][4 * q + 2] = sum.z;
-                acc[i][j][4 * q + 3] = sum.w;
+                const float4 t4 = sum[(i * FN + j) * 4 + q];
+                acc[i][j][4 * q] = t4.x;
+                acc[i][j][4 * q + 1] = t4.y;
+                acc[i][j][4 * q + 2] = t4.z;
+                acc[i][j][4 * q + 3] = t4.w;
             }
     write_tile<BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, w.pm * BM, w.pn * BN);
 }
