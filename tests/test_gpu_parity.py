@@ -253,6 +253,30 @@ def test_guard_bands_and_strided_c(in_dtype):
     assert torch.all(full[mask] == canary), "wrote outside C's view"
 
 
+@pytest.mark.parametrize("c_case", ["rows_aligned", "base_off", "stride_off"])
+def test_c_row_vector_stores(c_case):
+    """C as a view into a padded buffer: base and row stride 4-element aligned,
+    base off by two elements, row stride off by two elements. Every candidate
+    kernel and output dtype writes the view bit-exactly and nothing outside it
+    (interior and edge tiles, every store width)."""
+    M, N, K = 520, 584, 136  # several 256- and 64-wide interior tiles plus ragged edges
+    width, col = {"rows_aligned": (N + 12, 4), "base_off": (N + 12, 2), "stride_off": (N + 10, 4)}[c_case]
+    note(f"C row stores {c_case}: {M}x{N}x{K}, row stride {width}, column origin {col}")
+    a, b = inputs.integer_operands(M, N, K, "bf16", seed=61)
+    a_dev, b_dev = a.to(DEV), b.to(DEV)
+    for out in ("bf16", "f16", "f32"):
+        want = oracle.encode(ref_full(a, b, "bf16"), out)
+        for cfg in dg.candidates(dg.DG_BF16, CODE[out]):
+            c_big = torch.full((M + 2, width), float("nan"), dtype=TD[out], device=DEV)
+            c = c_big[1:1 + M, col:col + N]
+            dg.gemm_config(a_dev, b_dev, cfg, out=c, out_dtype=TD[out])
+            torch.cuda.synchronize()
+            assert_bits_equal(out_bits(c, out), want, f"{cfg} {c_case} -> {out}")
+            outside = torch.ones(M + 2, width, dtype=torch.bool)
+            outside[1:1 + M, col:col + N] = False
+            assert torch.isnan(c_big.float().cpu()[outside]).all(), f"{cfg} {c_case} -> {out}: wrote outside C"
+
+
 def test_transposed_c_and_transpose_identity():
     a, b = inputs.integer_operands(96, 160, 200, "bf16", seed=51)
     a_d, b_d = a.to(DEV), b.to(DEV)
