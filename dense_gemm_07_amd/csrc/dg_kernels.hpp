@@ -629,6 +629,45 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, co
     }
 }
 
+// The fused epilogue without LDS, for an interior tile whose epilogue needs
+// nothing from other lanes: no residual (beta == 0), bias absent or one per
+// column, no activation or ReLU. In the accumulator layout every register of
+// lane l in fragment column j lies in column col_base + 32j, so the lane loads
+// one bias value per fragment column and stores each element straight from its
+// register, as the plain store does (measured faster than staging the tile for
+// whole-row writes). Same arithmetic as epi_rows, absent terms as +0.
+template <typename TO, int FM, int FN>
+__device__ __forceinline__ void epi_direct_t(const GemmArgs &g, const EpiRows &e, const f32x16 (&acc)[FM][FN],
+                                             int row_base, int col_base) {
+    typename TO::storage *C = reinterpret_cast<typename TO::storage *>(e.C);  // this product's C
+    const bool relu = g.act == DG_ACT_RELU;
+    float bc[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        bc[j] = g.bias ? load_any(g.bias, e.b_off + (int64_t)(col_base + j * 32) * g.sbias, g.bias_dtype) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t cbase = (int64_t)(col_base + j * 32) * g.scn;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                float t = __builtin_fmaf(g.beta, 0.0f, g.alpha * acc[i][j][r]) + (bc[j] + 0.0f);
+                t = (relu && t < 0.0f) ? 0.0f : t;
+                C[(int64_t)gm * g.scm + cbase] = from_f32<TO>(t);
+            }
+        }
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void epi_direct(const GemmArgs &g, const EpiRows &e, const f32x16 (&acc)[FM][FN],
+                                           int row_base, int col_base) {
+    if (g.out_dtype == DG_BF16) epi_direct_t<BF16, FM, FN>(g, e, acc, row_base, col_base);
+    else if (g.out_dtype == DG_F16) epi_direct_t<F16, FM, FN>(g, e, acc, row_base, col_base);
+    else epi_direct_t<F32, FM, FN>(g, e, acc, row_base, col_base);
+}
+
 // The same tile through the fused epilogue, staged through LDS. The tile is
 // written to LDS (fp32, rows padded by 4 floats) in passes of whole 32-row
 // fragment blocks. Each thread then owns one 4-column group of the tile
@@ -684,11 +723,14 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
     e.rvec = e.ncols == 4 && e.use_r && g.srn == 1 && g.srm % 4 == 0 &&
              ((uintptr_t)g.R + (uintptr_t)((e.r_off + e.gn0) * r_es)) % (uintptr_t)(4 * r_es) == 0;
     e.rmode = (!e.rvec || r_es == 4) ? 0 : (g.r_dtype == DG_BF16 ? 1 : 2);
-    // One pass loop per pass size (compile-time, so the staging of each
-    // fragment block resolves statically): PRL when rows are requested ahead.
+    if (!e.use_r && !e.row_bias && g.act != DG_ACT_GELU && m0 + BM <= g.M && n0 + BN <= g.N) {
+        epi_direct<FM, FN>(g, e, acc, m0 + wm * WTM + 4 * (lane >> 5), n0 + wn * WTN + (lane & 31));
+        return;
+    }
+    // The pass loop; the pass size is a compile-time constant, so the staging
+    // of each fragment block resolves statically.
     auto passes = [&](auto pr_tag) {
         constexpr int PR = decltype(pr_tag)::value;
-        constexpr bool LOADS = PR == PRL && PRL != PRN;
         uint32_t raw[RU][2];
         float br[RU];
 #pragma unroll
@@ -697,7 +739,7 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
         for (int p0 = 0; p0 < BM; p0 += PR) {
             e.m_row0 = m0 + p0;
             e.rows = min(PR, g.M - m0 - p0);
-            if (LOADS || PRL == PRN) epi_load<RU>(g, e, raw, br);
+            epi_load<RU>(g, e, raw, br);
             __syncthreads();  // the previous pass (or the K loop) is done with the LDS
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -726,8 +768,13 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
             }
         }
     };
-    if (PRL == PRN || e.use_r || e.row_bias) passes(std::integral_constant<int, PRL>{});
-    else passes(std::integral_constant<int, PRN>{});
+    // Every epilogue stages PRL rows per pass. A variant that staged PRN rows
+    // (96 when that is below BM: 256x256x64 and 128x128x64 at 2 stages) when
+    // no rows were requested ahead wrote wrong values in about an eighth of
+    // the elements on the GPU (30 of 256 rows at 4096^3, varying counts at
+    // 128x128), while the same tiles staged PRL rows were exact; it is not
+    // compiled.
+    passes(std::integral_constant<int, PRL>{});
 }
 
 // ---- split-K -------------------------------------------------------------------

@@ -289,6 +289,18 @@ def test_epilogue_integers_bit_exact(case, layouts):
 
 
 @pytest.mark.parametrize("case", [c for c in EPI_CASES if c[0] != "f32"], ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("cfg_shape", [(256, 256, 64, 2), (128, 128, 64, 2), (256, 256, 32, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("layouts", [("row", "row"), ("mis", "col")], ids="/".join)
+def test_epilogue_large_tiles_bit_exact(case, cfg_shape, layouts):
+    """The epilogue of the large tiles, interior and edge (800 = 3 x 256 + 32),
+    through both kernels (direct-to-LDS, register-staged): their LDS holds
+    more rows per pass than the 64x64 tiles of the default choice at small
+    shapes."""
+    check_epilogue(800, 800, 256, case, layouts, cfg=config(case[0], *cfg_shape), seed=7)
+
+
+@pytest.mark.parametrize("case", [c for c in EPI_CASES if c[0] != "f32"], ids=lambda c: "-".join(map(str, c)))
 def test_epilogue_with_split_k(case):
     for cfg_shape, splits in [((64, 64, 64, 4), 3), ((256, 256, 64, 2), 5)]:
         cfg = config(case[0], *cfg_shape, splits=splits)
