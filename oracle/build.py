@@ -14,13 +14,16 @@ LIB = os.path.join(HERE, "libref_gemm.so")
 
 
 def build(verbose: bool = False) -> str:
+    # A temporary name per process: concurrent builds (parallel test workers)
+    # each rename a complete library into place.
+    tmp = f"{LIB}.tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
            "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-           "-o", LIB + ".tmp", SRC, "-lm"]
+           "-o", tmp, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(tmp, LIB)
     return LIB
 
 
