@@ -14,6 +14,14 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
 
 
+def _number(text):
+    """An integer where the text is one, else a float (decimal fixtures)."""
+    try:
+        return int(text)
+    except ValueError:
+        return float(text)
+
+
 def load_golden(name):
     """Parse a fixture: blocks of `LABEL rows cols` followed by rows of numbers."""
     blocks = {}
@@ -23,7 +31,7 @@ def load_golden(name):
     while i < len(lines):
         label, r, c = lines[i].split()
         r, c = int(r), int(c)
-        rows = [[int(x) for x in lines[i + 1 + t].split()] for t in range(r)]
+        rows = [[_number(x) for x in lines[i + 1 + t].split()] for t in range(r)]
         assert all(len(row) == c for row in rows), (name, label)
         blocks[label] = rows
         i += 1 + r

@@ -518,3 +518,31 @@ def test_attention_one_hot_limit_and_large_scores(oracle_mod):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     assert np.allclose(o[0, 0], np.broadcast_to(oracle_mod.decode(vb[0, 0, 2], "f16"), (3, D)), rtol=0, atol=1e-300)
     assert np.allclose(lse[0, 0], 1024.0, rtol=1e-15, atol=0)  # the other keys add exp(-1024) ~ 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_attention_hand_worked_softmax_weights(oracle_mod, dtype):
+    """Scaled scores (0, 1, 2) against one-hot values: O holds the softmax weights themselves,
+    which the fixture gives as hand-derived numbers (logistic at +-1, softmax of (0, 1, 2)).
+    Fails for a softmax in another base, a missing or doubled 1/sqrt(head_dim) scale, a
+    causal mask off by one, or lse without the row maximum."""
+    g = load_golden("attention_softmax_hand.txt")
+
+    def bits(rows):
+        t = torch.tensor(rows, dtype=torch.float32).to(inputs.TORCH_DTYPES[dtype])
+        return np.ascontiguousarray(inputs.bits(t, dtype).reshape(1, 1, len(rows), -1))
+
+    q, k, v = bits(g["Q"]), bits(g["K"]), bits(g["V"])
+    D = q.shape[-1]
+    for causal, tag, nk in ((True, "CAUSAL", 3), (False, "FULL", 3), (False, "TWO", 2)):
+        o, lse = oracle_mod.attention(q, np.ascontiguousarray(k[:, :, :nk]), np.ascontiguousarray(v[:, :, :nk]),
+                                      dtype, causal=causal)
+        want_o = np.zeros((3, D))
+        want_o[:, :nk] = np.array(g[f"O_{tag}"], dtype=np.float64)
+        assert np.allclose(o[0, 0], want_o, rtol=0, atol=2e-16), (tag, o[0, 0, :, :3])
+        assert np.allclose(lse[0, 0], np.array(g[f"LSE_{tag}"], dtype=np.float64)[:, 0], rtol=0, atol=5e-16), tag
+    # The same weights with the scale given explicitly: K doubled and scale 1/8.
+    k2 = bits([[2 * x for x in row] for row in g["K"]])
+    o, lse = oracle_mod.attention(q, k2, v, dtype, scale=0.125, causal=True)
+    assert np.allclose(o[0, 0, :, :3], np.array(g["O_CAUSAL"], dtype=np.float64), rtol=0, atol=2e-16)
+    assert np.allclose(lse[0, 0], np.array(g["LSE_CAUSAL"], dtype=np.float64)[:, 0], rtol=0, atol=5e-16)
