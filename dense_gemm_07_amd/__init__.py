@@ -284,18 +284,28 @@ def cache_load(path):
 
 # ---- dg_gemm_ex: fused epilogue, strided batch, split-K ------------------------
 
-# Split-K workspace the binding keeps per device, grown on demand.
+# Split-K workspace the binding keeps per (device, stream), grown on demand.
+# One buffer per stream: two split-K calls on different streams would otherwise
+# write their partial tiles into the same memory at the same time. Each buffer
+# is allocated while its stream is current, so torch's caching allocator ties
+# it to that stream: when a grown buffer replaces it, the old memory is handed
+# out again only to later work on the same stream, which runs after every
+# kernel already queued there that reads it.
 DEFAULT_WORKSPACE_BYTES = 64 << 20
 _workspaces = {}
 
 
-def _workspace(t, nbytes):
-    """The cached split-K workspace of tensor t's GPU (grown to nbytes if needed)."""
-    key = t.get_device()
+def _workspace(t, nbytes, stream):
+    """The cached split-K workspace for t's GPU and `stream` (a raw HIP stream
+    handle, ctypes.c_void_p), grown to nbytes if needed."""
+    key = (t.get_device(), stream.value or 0)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         import torch
-        ws = torch.empty(max(nbytes, DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=f"cuda:{key}")
+        dev = torch.device("cuda", key[0])
+        s = torch.cuda.ExternalStream(key[1], device=dev) if key[1] else torch.cuda.default_stream(dev)
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(nbytes, DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -391,15 +401,16 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
     out = _ex_out(a, b, out, out_dtype)
     prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
     ws_ptr, ws_bytes = None, 0
+    raw = _stream(a, stream)
     if workspace is True:
         need = 0
         if config is not None and config.k_splits > 1:
             need = workspace_size(prob[0], prob[1], prob[2], batch.count, config)
-        ws = _workspace(a, need)
+        ws = _workspace(a, need, raw)
         ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     elif workspace is not None and workspace is not False:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(library().dg_gemm_ex(*prob, _stream(a, stream), ctypes.byref(epi), ctypes.byref(batch),
+    _check(library().dg_gemm_ex(*prob, raw, ctypes.byref(epi), ctypes.byref(batch),
                                 ctypes.byref(config) if config is not None else None, ws_ptr, ws_bytes))
     return out
 
@@ -410,13 +421,14 @@ def autotune_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual
     out = _ex_out(a, b, out, out_dtype)
     prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
     ws_ptr, ws_bytes = None, 0
+    raw = _stream(a, stream)
     if workspace is True:
-        ws = _workspace(a, 0)
+        ws = _workspace(a, 0, raw)
         ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     elif workspace is not None and workspace is not False:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     cfg, ms = Config(), ctypes.c_float()
-    _check(library().dg_autotune_ex(*prob, _stream(a, stream), ctypes.byref(epi), ctypes.byref(batch), ws_ptr,
+    _check(library().dg_autotune_ex(*prob, raw, ctypes.byref(epi), ctypes.byref(batch), ws_ptr,
                                     ws_bytes, repeats, ctypes.byref(cfg), ctypes.byref(ms)))
     return cfg, ms.value
 

@@ -120,6 +120,28 @@ bool batch_disjoint(const Problem &p) {
     return nested({{p.M, p.scm}, {p.N, p.scn}, {p.batch, p.bsc}});
 }
 
+// Byte range [lo, hi) that a strided batch of M x N views touches.
+std::pair<i128, i128> byte_span(const void *base, int64_t batch, int64_t bs, int64_t M, int64_t sm, int64_t N,
+                                int64_t sn, int es) {
+    const i128 elems = (i128)(batch - 1) * bs + (i128)(M - 1) * sm + (i128)(N - 1) * sn + 1;
+    const i128 lo = (i128)(uintptr_t)base;
+    return {lo, lo + elems * es};
+}
+
+// The residual is C's own view: same address, dtype, strides and batch stride.
+bool same_view_as_c(const Problem &p) {
+    const Epi &e = p.epi;
+    return e.R == p.C && e.r_dtype == p.out && e.srm == p.scm && e.srn == p.scn && (p.batch <= 1 || p.bsr == p.bsc);
+}
+
+bool spans_overlap(const Problem &p) {
+    const Epi &e = p.epi;
+    const int64_t nb = p.batch < 1 ? 1 : p.batch;
+    const auto c = byte_span(p.C, nb, p.bsc, p.M, p.scm, p.N, p.scn, elem_size(p.out));
+    const auto r = byte_span(e.R, nb, p.bsr, p.M, e.srm, p.N, e.srn, elem_size(e.r_dtype));
+    return c.first < r.second && r.first < c.second;
+}
+
 dg_status validate_ex(const Problem &p) {
     const bool c_used = p.M > 0 && p.N > 0 && p.batch > 0;
     if (p.batch < 0) return fail(DG_ERR_INVALID_VALUE, "negative batch count");
@@ -137,6 +159,13 @@ dg_status validate_ex(const Problem &p) {
         if (e.srm < 0 || e.srn < 0) return fail(DG_ERR_INVALID_VALUE, "negative residual stride");
         if ((uintptr_t)e.R % (uintptr_t)elem_size(e.r_dtype))
             return fail(DG_ERR_INVALID_VALUE, "residual not aligned to its element size");
+        // A residual that shares memory with C must be C itself, element for
+        // element (the in-place C = alpha*AB + beta*C): each workgroup then
+        // reads only the elements it writes. Any other overlap would let one
+        // workgroup read what another tile's workgroup is writing.
+        if (p.C && !same_view_as_c(p) && spans_overlap(p))
+            return fail(DG_ERR_INVALID_VALUE,
+                        "residual overlaps C without being C (same pointer, dtype, strides and batch stride)");
     }
     if (e.bias && c_used) {
         if (!dtype_ok(e.bias_dtype)) return fail(DG_ERR_INVALID_VALUE, "unknown bias dtype %d", e.bias_dtype);

@@ -738,7 +738,11 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
 #pragma unroll 1
         for (int p0 = 0; p0 < BM; p0 += PR) {
             e.m_row0 = m0 + p0;
-            e.rows = min(PR, g.M - m0 - p0);
+            // Rows of this pass inside the tile and inside C. The tile bound
+            // matters when PR does not divide BM: the last pass then holds
+            // fewer than PR rows, and the rows past the tile belong to the
+            // next tile's workgroup.
+            e.rows = min(min(PR, BM - p0), g.M - m0 - p0);
             epi_load<RU>(g, e, raw, br);
             __syncthreads();  // the previous pass (or the K loop) is done with the LDS
 #pragma unroll
@@ -768,12 +772,16 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
             }
         }
     };
-    // Every epilogue stages PRL rows per pass. A variant that staged PRN rows
-    // (96 when that is below BM: 256x256x64 and 128x128x64 at 2 stages) when
-    // no rows were requested ahead wrote wrong values in about an eighth of
-    // the elements on the GPU (30 of 256 rows at 4096^3, varying counts at
-    // 128x128), while the same tiles staged PRL rows were exact; it is not
-    // compiled.
+    // Every epilogue stages PRL rows per pass (a divisor of BM; 64 on the
+    // 128- and 256-row tiles). An earlier variant staged PRN = 96 rows per pass on
+    // 256x256 and 128x128 tiles and bounded a pass's rows by C only, not by
+    // the tile: its last pass (rows 192..287 of a 256-row tile, 96..191 of a
+    // 128-row tile) wrote stale staged rows into the first 32 or 64 rows of
+    // the next tile down, racing with that tile's own workgroup. That is the
+    // 15/128 of C it got wrong at 4096^3 (15 of 16 tile rows spill 32 rows
+    // each) and the run-to-run variation at 128x128. The bound above closes
+    // it for any pass size.
+    static_assert(BM % PRL == 0, "whole passes: the pass loop covers the tile exactly");
     passes(std::integral_constant<int, PRL>{});
 }
 

@@ -107,10 +107,19 @@ typedef struct dg_config {
 /*
  * C = A @ B with the library's choice of kernel: the cached config for this
  * problem key if one exists (see dg_autotune), else a built-in heuristic.
+ * This is the pages' host wrapper, which checks the shapes, computes the
+ * grid from the block sizes and launches the kernel ("用 Triton 写 GPU
+ * Kernel：从 Vector Add、Softmax 到 MatMul" §4.5; the kernel's runtime arguments
+ * are the pointers, M, N, K and the strides of "Triton：04 Matmul、Autotune 与
+ * PyTorch 集成", its teaching kernel), with C supplied by the caller.
  * Never benchmarks, so its cost is one kernel launch (unless the
- * environment sets DG_AUTOTUNE_ON_MISS=1, which autotunes on a cache miss).
+ * environment sets DG_AUTOTUNE_ON_MISS=1, which autotunes on a cache miss,
+ * as the pages' first call does).
  * Arguments: problem sizes; the three device pointers and their element
  * strides; the input dtype (shared by A and B) and the output dtype; stream.
+ * Errors: DG_ERR_INVALID_VALUE / DG_ERR_UNSUPPORTED from the checks listed
+ * at the top of this file, DG_ERR_HIP if the launch fails; nothing is
+ * enqueued on error.
  */
 dg_status dg_gemm(int64_t M, int64_t N, int64_t K,
                   const void *A, int64_t stride_am, int64_t stride_ak,
@@ -119,10 +128,16 @@ dg_status dg_gemm(int64_t M, int64_t N, int64_t K,
                   dg_dtype in_dtype, dg_dtype out_dtype, void *stream);
 
 /*
- * Same as dg_gemm with an explicit configuration (tests, ablations). A
- * config that names no compiled kernel, or one that cannot run this
+ * Same as dg_gemm with an explicit configuration (tests, ablations): one
+ * point of the autotune space, i.e. the block sizes, warps (here waves) and
+ * pipeline stages that a configuration fixes ("Triton：04 Matmul、Autotune 与
+ * PyTorch 集成", the section on what autotune chooses; "I Wrote a GPU Matmul
+ * Kernel From Scratch in Triton", Step 3, which launches with one fixed block
+ * size). A config that names no compiled kernel, or one that cannot run this
  * problem's dtype pair, returns DG_ERR_NO_CONFIG. The problem size is never
- * a reason to reject a config: ragged edges and K < block_k are masked.
+ * a reason to reject a config: ragged edges and K < block_k are masked
+ * ("用 Triton 写 GPU Kernel：从 Vector Add、Softmax 到 MatMul" §4.5-§4.6, the
+ * masked loads and store).
  */
 dg_status dg_gemm_config(int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t stride_am, int64_t stride_ak,
@@ -255,7 +270,11 @@ dg_status dg_autotune_ex(int64_t M, int64_t N, int64_t K,
 
 /*
  * Workspace bytes config `cfg` needs for an M x N x K problem with
- * `batch_count` products: 0 when it does not split K, else one fp32 partial
+ * `batch_count` products. Split-K rests on the K slices of one output tile
+ * adding up to its value in any grouping ("用 Triton 写 GPU Kernel：从 Vector
+ * Add、Softmax 到 MatMul" §3.3, where tile (0, 0) is the sum of two K-slice
+ * partials); each range's partial tile is kept here until it is summed.
+ * Sizes: 0 when it does not split K, else one fp32 partial
  * tile per (product, tile, K range) = tiles * batch_count * ranges *
  * block_m * block_n * 4. K is cut into ranges of k_chunk = block_k *
  * ceil(ceil(K / k_splits) / block_k) elements; the ranges actually used
@@ -303,7 +322,13 @@ dg_status dg_attention_fwd(int64_t batch, int64_t heads, int64_t seq_q, int64_t 
  * inspected for alignment (they may be NULL: then taken as 16-byte aligned).
  * *from_cache (may be NULL) is set to 1 if the config came from the cache.
  * The cache key is (M, N, K) plus the dtypes, each operand's layout class
- * and the vector-alignment class.
+ * and the vector-alignment class: the pages key the tuned choice on M, N and
+ * K and tune again when any of them changes ("I Wrote a GPU Matmul Kernel
+ * From Scratch in Triton", Step 5), and keep the winner per input size
+ * ("Triton：04 Matmul、Autotune 与 PyTorch 集成", the section on what autotune
+ * chooses). A miss falls back to a heuristic, since different shapes want
+ * different configs (same page, the section on why shapes need different
+ * configs).
  */
 dg_status dg_select_config(int64_t M, int64_t N, int64_t K,
                            const void *A, int64_t stride_am, int64_t stride_ak,
@@ -315,7 +340,8 @@ dg_status dg_select_config(int64_t M, int64_t N, int64_t K,
 /*
  * The config dg_gemm_ex would use with cfg == NULL for this batch (NULL: one
  * product) and a workspace of workspace_bytes (split-K is chosen only when
- * its workspace fits), without any GPU work. Pointers as dg_select_config.
+ * its workspace fits), without any GPU work. Pointers, key and citations as
+ * dg_select_config; the batch count is part of the key.
  */
 dg_status dg_select_config_ex(int64_t M, int64_t N, int64_t K,
                               const void *A, int64_t stride_am, int64_t stride_ak,
@@ -324,11 +350,26 @@ dg_status dg_select_config_ex(int64_t M, int64_t N, int64_t K,
                               dg_dtype in_dtype, dg_dtype out_dtype, const dg_batch *batch,
                               int64_t workspace_bytes, dg_config *out, int32_t *from_cache);
 
-/* Autotune candidates for a dtype pair: count, and the i-th (0-based). */
+/*
+ * Autotune candidates for a dtype pair: count, and the i-th (0-based). The
+ * pages tune over an explicit list of configs ("I Wrote a GPU Matmul Kernel
+ * From Scratch in Triton", Step 5, fifteen of them) and note that autotune
+ * can only pick among the candidates it is given ("Triton：04 Matmul、Autotune
+ * 与 PyTorch 集成", the second common mistake). dg_get_candidate returns
+ * DG_ERR_INVALID_VALUE for an index outside [0, count) or an unknown dtype;
+ * dg_num_candidates returns 0 for an unknown dtype.
+ */
 int32_t dg_num_candidates(dg_dtype in_dtype, dg_dtype out_dtype);
 dg_status dg_get_candidate(int32_t i, dg_dtype in_dtype, dg_dtype out_dtype, dg_config *out);
 
-/* Check a full argument list exactly as dg_gemm does, without launching. */
+/*
+ * Check a full argument list exactly as dg_gemm does, without launching. The
+ * pages' wrapper asserts that the inner dimensions agree and the inputs are
+ * contiguous before it launches ("用 Triton 写 GPU Kernel：从 Vector Add、
+ * Softmax 到 MatMul" §4.5); here a failed check is a status code (DG_OK or
+ * DG_ERR_INVALID_VALUE / DG_ERR_UNSUPPORTED) plus dg_last_error(), and any
+ * strides are accepted as long as C's index map is injective.
+ */
 dg_status dg_validate(int64_t M, int64_t N, int64_t K,
                       const void *A, int64_t stride_am, int64_t stride_ak,
                       const void *B, int64_t stride_bk, int64_t stride_bn,
@@ -353,13 +394,32 @@ dg_status dg_tile_coords(int32_t grid_m, int32_t grid_n, int32_t group_m, int32_
 dg_status dg_grid_shape(int64_t M, int64_t N, int64_t K, const dg_config *cfg,
                         int64_t *grid_m, int64_t *grid_n, int64_t *k_steps);
 
-/* Config cache: clear; save to / load from a text file (one key per line). */
+/*
+ * Config cache: the winners of dg_autotune / dg_autotune_ex under their keys
+ * (the pages cache the fastest config per key, so that only the first call
+ * at a shape pays for the benchmark: "I Wrote a GPU Matmul Kernel From
+ * Scratch in Triton", Step 5; "Triton：04 Matmul、Autotune 与 PyTorch 集成", the
+ * section on what autotune chooses). dg_cache_clear empties it;
+ * dg_cache_save writes it to a text file (a header line, then one key and
+ * config per line) and dg_cache_load merges such a file into it, skipping
+ * malformed lines (their count goes to dg_last_error). Save/load return
+ * DG_ERR_INVALID_VALUE for a NULL path, a file that cannot be opened or
+ * written, or a file without the header. dg_cache_size counts the entries.
+ * Mutex-guarded; the cache lives in host memory for the process.
+ */
 dg_status dg_cache_clear(void);
 dg_status dg_cache_save(const char *path);
 dg_status dg_cache_load(const char *path);
 int32_t dg_cache_size(void);
 
-/* Static description of a status code, and the calling thread's last error. */
+/*
+ * Static description of a status code, and the calling thread's last error
+ * (an empty string after a successful call). The pages stop a bad call with
+ * an assert ("用 Triton 写 GPU Kernel：从 Vector Add、Softmax 到 MatMul" §4.5);
+ * a C library returns the status instead and keeps the detail here. Both
+ * strings are owned by the library: the first is static, the second valid
+ * until the thread's next call into the library.
+ */
 const char *dg_status_string(dg_status s);
 const char *dg_last_error(void);
 

@@ -166,6 +166,30 @@ def test_split_k_deterministic_and_workspace_needs_no_init():
     assert_within_tol(got, ref, epilogue_tolerance(K, "bf16", "bf16", got, ref, 1.0, np.abs(ref), "none"), "split")
 
 
+def test_split_k_workspace_per_stream():
+    """The binding's cached workspace is one buffer per (device, stream): split-K
+    calls queued on two streams at once write their partial tiles into
+    different memory, and both results are exact (integers)."""
+    M, N, K = 200, 136, 4096
+    cfg = config("bf16", 64, 64, 64, stages=4, splits=8)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    ops = [inputs.integer_operands(M, N, K, "bf16", seed=s) for s in (31, 32)]
+    wants = [oracle.encode(ref_product(a, b, "bf16"), "f32") for a, b in ops]
+    dev = [(a.to(DEV), b.to(DEV)) for a, b in ops]
+    outs = [torch.empty(M, N, dtype=torch.float32, device=DEV) for _ in ops]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        note(f"two streams, rep {rep}")
+        for (ad, bd), c, st in zip(dev, outs, (s1, s2)):
+            dg.gemm_ex(ad, bd, out=c, config=cfg, stream=st)
+        torch.cuda.synchronize()
+        for c, want in zip(outs, wants):
+            assert_bits_equal(out_bits(c, "f32"), want, f"stream rep {rep}")
+    key = lambda st: (torch.device(DEV).index or 0, st.cuda_stream)
+    w1, w2 = dg._workspaces[key(s1)], dg._workspaces[key(s2)]
+    assert w1.data_ptr() != w2.data_ptr()
+
+
 def test_split_k_counts_beyond_k_slices():
     """More splits than K slices: the ranges collapse to the non-empty ones."""
     M, N, K = 70, 90, 100  # two 64-slices

@@ -253,6 +253,21 @@ def test_gemm_ex_rejects_bad_epilogue():
     assert b"residual" in dg.library().dg_last_error()
 
 
+def test_gemm_ex_rejects_residual_overlapping_c():
+    """A residual that shares memory with C must be C's own view; any other
+    overlap lets one tile's workgroup read what another is writing."""
+    def status(res, rdt, srm, srn, batch=None):
+        return gemm_ex_status(epi=dg.Epilogue(alpha=1.0, beta=1.0, residual=res, residual_dtype=rdt,
+                                              stride_rm=srm, stride_rn=srn), batch=batch)
+    assert status(FAKE, BF16, 1, 64) == INVALID            # C transposed
+    assert b"overlaps C" in dg.library().dg_last_error()
+    assert status(FAKE + 128, BF16, 64, 1) == INVALID      # C one row down
+    assert status(FAKE - 2, BF16, 64, 1) == INVALID        # C one element left
+    assert status(FAKE, F32, 32, 1) == INVALID             # same bytes read as fp32
+    # C's first product broadcast to the whole batch while C has two products
+    assert status(FAKE, BF16, 64, 1, dg.Batch(count=2, stride_c=4096, stride_r=0)) == INVALID
+
+
 def test_gemm_ex_rejects_bad_batch():
     assert gemm_ex_status(batch=dg.Batch(count=-1)) == INVALID
     assert gemm_ex_status(batch=dg.Batch(count=2, stride_a=-8)) == INVALID
