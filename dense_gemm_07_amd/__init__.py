@@ -19,7 +19,7 @@ from .build import LIB
 
 __all__ = [
     "Config", "DGError", "gemm", "gemm_config", "autotune", "select_config", "candidates",
-    "Epilogue", "Batch", "gemm_ex", "autotune_ex", "workspace_size", "select_config_ex", "matmul", "linear",
+    "Epilogue", "Batch", "gemm_ex", "gemm_ex_noalloc", "autotune_ex", "workspace_size", "select_config_ex", "matmul", "linear",
     "attention",
     "validate", "tile_coords", "grid_shape", "cache_clear", "cache_save", "cache_load",
     "cache_size", "library", "DG_F32", "DG_F16", "DG_BF16", "VARIANT_SIMT", "VARIANT_MFMA",
@@ -87,6 +87,8 @@ def library():
         lib.dg_validate.argtypes = _PROBLEM
         lib.dg_gemm_ex.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch),
                                               ctypes.POINTER(Config), _p, _i64]
+        lib.dg_gemm_ex_noalloc.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch),
+                                                      ctypes.POINTER(Config)]
         lib.dg_autotune_ex.argtypes = _PROBLEM + [_p, ctypes.POINTER(Epilogue), ctypes.POINTER(Batch), _p, _i64,
                                                   _i32, ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_float)]
         lib.dg_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(Config), ctypes.POINTER(_i64)]
@@ -105,7 +107,7 @@ def library():
         lib.dg_last_error.restype = ctypes.c_char_p
         for name in ("dg_gemm", "dg_gemm_config", "dg_autotune", "dg_select_config", "dg_select_config_ex",
                      "dg_validate",
-                     "dg_gemm_ex", "dg_autotune_ex", "dg_workspace_size", "dg_attention_fwd",
+                     "dg_gemm_ex", "dg_gemm_ex_noalloc", "dg_autotune_ex", "dg_workspace_size", "dg_attention_fwd",
                      "dg_get_candidate", "dg_tile_coords", "dg_grid_shape", "dg_cache_clear",
                      "dg_cache_save", "dg_cache_load"):
             getattr(lib, name).restype = ctypes.c_int
@@ -292,6 +294,7 @@ def cache_load(path):
 # out again only to later work on the same stream, which runs after every
 # kernel already queued there that reads it.
 DEFAULT_WORKSPACE_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 32 << 20  # DG_NOALLOC_SCRATCH_BYTES of include/dg.h
 _workspaces = {}
 
 
@@ -412,6 +415,18 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(library().dg_gemm_ex(*prob, raw, ctypes.byref(epi), ctypes.byref(batch),
                                 ctypes.byref(config) if config is not None else None, ws_ptr, ws_bytes))
+    return out
+
+
+def gemm_ex_noalloc(a, b, out, *, alpha=1.0, beta=0.0, residual=None, bias=None, bias_per_row=False,
+                    activation=None, config=None, stream=None):
+    """dg_gemm_ex_noalloc: gemm_ex with split-K partials in the library's fixed
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES), so neither the library nor this
+    call allocates device memory; `out` must be given. Calls that overlap in
+    time on one GPU share the scratch and race."""
+    prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
+    _check(library().dg_gemm_ex_noalloc(*prob, _stream(a, stream), ctypes.byref(epi), ctypes.byref(batch),
+                                        ctypes.byref(config) if config is not None else None))
     return out
 
 

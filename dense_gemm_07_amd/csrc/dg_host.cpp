@@ -662,6 +662,44 @@ dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_co
 }  // namespace
 }  // namespace dg
 
+// ---- scratch of the allocation-free entry point ---------------------------------
+// Split-K partial tiles of dg_gemm_ex_noalloc live in this array: one copy per
+// GPU, created when the library's code object is loaded on that GPU and held
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[DG_NOALLOC_SCRATCH_BYTES];
+
+namespace dg {
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch;  // device -> address of its copy of `scratch`
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device). No allocation: the array is part of the loaded code object.
+dg_status scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DG_ERR_HIP, "hipGetSymbolAddress of the scratch array on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        it = g_scratch.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return DG_OK;
+}
+
+}  // namespace
+}  // namespace dg
+
 using namespace dg;
 
 extern "C" {
@@ -760,6 +798,33 @@ dg_status dg_gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam
     const dg_config c = cfg ? *cfg : choose(p, workspace_bytes);
     if (!cfg) log_choice("gemm_ex", p, c);
     return launch(p, c, (hipStream_t)stream, workspace, workspace_bytes);
+}
+
+dg_status dg_gemm_ex_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak,
+                             const void *B, int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn,
+                             dg_dtype in_dtype, dg_dtype out_dtype, void *stream, const dg_epilogue *epilogue,
+                             const dg_batch *batch, const dg_config *cfg) {
+    g_last_error.clear();
+    Problem p = make_problem(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype);
+    apply_ex(p, epilogue, batch);
+    dg_status s = validate(p);
+    if (s != DG_OK) return s;
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return DG_OK;
+    const int64_t cap = DG_NOALLOC_SCRATCH_BYTES;
+    const dg_config c = cfg ? *cfg : choose(p, cap);
+    if (c.k_splits > 1) {
+        const WsLayout L = ws_layout(p.M, p.N, p.batch, c, split_plan(p.K, c).splits);
+        if (L.total < 0 || L.total > cap)
+            return fail(DG_ERR_UNSUPPORTED,
+                        "split-K partials of this call need %" PRId64 " bytes of scratch; the allocation-free "
+                        "entry point holds at most %" PRId64 " bytes",
+                        L.total, cap);
+    }
+    void *ws = nullptr;
+    s = scratch_address(&ws);
+    if (s != DG_OK) return s;
+    if (!cfg) log_choice("gemm_ex_noalloc", p, c);
+    return launch(p, c, (hipStream_t)stream, ws, cap);
 }
 
 dg_status dg_attention_fwd(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_kv, int64_t head_dim,

@@ -251,6 +251,34 @@ dg_status dg_gemm_ex(int64_t M, int64_t N, int64_t K,
                      const dg_config *cfg, void *workspace, int64_t workspace_bytes);
 
 /*
+ * dg_gemm_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments and results as dg_gemm_ex, without the workspace: split-K
+ * partial tiles go to a scratch array inside the library, a file-scope
+ * device array of DG_NOALLOC_SCRATCH_BYTES per GPU that exists from the
+ * library's load until the process ends. Nothing is allocated or freed.
+ *  - cfg == NULL: the library's choice, as dg_gemm_ex with a workspace of
+ *    DG_NOALLOC_SCRATCH_BYTES (it splits K only when the partials fit).
+ *  - An explicit cfg whose partials need more than DG_NOALLOC_SCRATCH_BYTES
+ *    (dg_workspace_size) returns DG_ERR_UNSUPPORTED and enqueues nothing.
+ *  - Every call on one GPU shares that GPU's scratch. Calls whose split-K
+ *    work overlaps in time on one GPU (different streams or threads without
+ *    synchronisation) race and give wrong results: issue them on one stream
+ *    or synchronise. The partials need no initialisation (each is written
+ *    before it is read, within the call).
+ *  - The first call on a device looks up that device's copy of the array
+ *    (hipGetSymbolAddress with the device current); DG_ERR_HIP if it fails.
+ */
+#define DG_NOALLOC_SCRATCH_BYTES (32 << 20)
+dg_status dg_gemm_ex_noalloc(int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t stride_am, int64_t stride_ak,
+                             const void *B, int64_t stride_bk, int64_t stride_bn,
+                             void *C, int64_t stride_cm, int64_t stride_cn,
+                             dg_dtype in_dtype, dg_dtype out_dtype, void *stream,
+                             const dg_epilogue *epilogue, const dg_batch *batch,
+                             const dg_config *cfg);
+
+/*
  * dg_autotune for a dg_gemm_ex problem (epilogue and batch included in every
  * timed launch). With a workspace, the candidates also include split-K
  * counts (2, 4, 8, 16) for tile shapes that do not fill the GPU. The winner
