@@ -279,7 +279,8 @@ def main():
     ap.add_argument("--split-k", action="store_true",
                     help="time dg_gemm_ex with a workspace (the library may split K)")
     ap.add_argument("--config", default="",
-                    help="time an explicit kernel config BMxBNxBK:waves:stages:group_m:xcd_remap (ablations)")
+                    help="time an explicit kernel config BMxBNxBK:waves:stages:group_m:xcd_remap[:k_splits] "
+                         "(ablations; k_splits > 1 with --split-k)")
     ap.add_argument("--misalign-a", action="store_true",
                     help="view A one element past a 16-byte boundary (forces the register-staged kernel)")
     ap.add_argument("--rotate", type=int, default=1, metavar="SETS",
@@ -369,14 +370,17 @@ def main():
         tune_s = time.perf_counter() - t0
     explicit = None
     if args.config:
-        shape, waves, stages, group_m, xcd = args.config.split(":")
+        shape, waves, stages, group_m, xcd, *more = args.config.split(":")
         bm, bn, bk = (int(x) for x in shape.split("x"))
         explicit = next((k for k in dg.candidates(dg._dtype_code(a.dtype), dg._dtype_code(c.dtype))
                          if (k.block_m, k.block_n, k.block_k, k.waves, k.stages) ==
                          (bm, bn, bk, int(waves), int(stages))), None)
         if explicit is None:
             raise SystemExit(f"no compiled kernel {args.config}")
-        explicit.group_m, explicit.xcd_remap, explicit.k_splits = int(group_m), int(xcd), 1
+        explicit.group_m, explicit.xcd_remap = int(group_m), int(xcd)
+        explicit.k_splits = int(more[0]) if more else 1
+        if explicit.k_splits > 1 and not args.split_k:
+            raise SystemExit("a config with k_splits > 1 needs --split-k (the workspace)")
     if explicit is not None:
         cfg = explicit
     elif ex:

@@ -272,6 +272,11 @@ std::pair<int, int> mfma_modes(const Problem &p) {
     const int sa = staged_mode(p.M, p.K, p.sam, p.sak);
     const int sb = staged_mode(p.N, p.K, p.sbn, p.sbk);
     if (sa == LD_GN || sb == LD_GN) return {LD_GN, LD_GN};
+    // The contiguous register-staged loads fetch every chunk as 16 bytes from
+    // inside the operand, clamped at its edges: a k-contiguous operand needs
+    // K >= 8, a row-contiguous one at least 8 rows.
+    if ((sa == LD_KU || sb == LD_KU) && p.K < 8) return {LD_GN, LD_GN};
+    if ((sa == LD_RU && p.M < 8) || (sb == LD_RU && p.N < 8)) return {LD_GN, LD_GN};
     return {sa, sb};
 }
 

@@ -285,6 +285,18 @@ __device__ __forceinline__ u32x4 load16_unaligned(const uint16_t *p) {
     return u32x4{v.x, v.y, v.z, v.w};
 }
 
+// Drops the first `sh` 16-bit elements of an 8-element chunk (element 0 is
+// the lowest 16 bits) and fills the top with zeros; sh >= 8 gives zero.
+__device__ __forceinline__ u32x4 drop_elems(u32x4 v, int sh) {
+    const uint64_t lo = ((uint64_t)v.y << 32) | v.x, hi = ((uint64_t)v.w << 32) | v.z;
+    const int s = 16 * min(sh, 8);  // 0..128 bits
+    const uint64_t lo_a = s == 0 ? lo : ((lo >> (s & 63)) | (hi << ((64 - s) & 63)));  // s < 64
+    const uint64_t lo_b = hi >> ((s - 64) & 63);                                        // 64 <= s < 128
+    const uint64_t nlo = s < 64 ? lo_a : (s < 128 ? lo_b : 0);
+    const uint64_t nhi = s < 64 ? (hi >> (s & 63)) : 0;
+    return u32x4{(uint32_t)nlo, (uint32_t)(nlo >> 32), (uint32_t)nhi, (uint32_t)(nhi >> 32)};
+}
+
 // Fetches one operand tile (ROWS x BK, rows = M for A or N for B) from
 // global memory into registers, then writes it to LDS as [ROWS][LDK] with k
 // contiguous. Elements outside the operand's view (row >= rows_valid or
@@ -443,6 +455,66 @@ struct TileLoader {
     }
 };
 
+
+// The loads of a k-contiguous operand tile (any element alignment) for the
+// deep pipeline of the small register-staged tiles: P register sets, every
+// chunk one 16-byte load with no branch, for any slice (also past K). The
+// thread's chunk rows are clamped to the tile's last valid row and k to
+// K - 8 (the caller guarantees that the operand has at least 8 columns, so
+// k = K - 8 relative to a K range still lies inside the row); store() undoes
+// both clamps: a chunk cut by K drops the elements it read before its own
+// k, chunks past K and rows past the valid ones become zeros.
+template <int ROWS, int BK, int LDK, int T, int P>
+struct KuStream {
+    static constexpr int KCH = BK / 8;      // 8-element k-chunks per row
+    static constexpr int NCH = ROWS * KCH;  // chunks per tile
+    static constexpr int PER = (NCH + T - 1) / T;
+    u32x4 reg[P][PER];
+    const uint16_t *row[PER];  // element (clamped row, k = chunk's k) of the operand
+    int kmax;                  // K - 8
+    int rows_valid;
+
+    __device__ __forceinline__ void init(const uint16_t *base, int64_t srow, int rows, int K, int tid) {
+        kmax = K - 8;
+        rows_valid = rows;
+#pragma unroll
+        for (int c = 0; c < PER; ++c) {
+            const int q = c * T + tid;
+            const int r = q / KCH;
+            const int rr = r < rows ? r : rows - 1;
+            row[c] = base + (int64_t)rr * srow;
+        }
+    }
+    __device__ __forceinline__ void load(int set, int tid, int k0) {
+#pragma unroll
+        for (int c = 0; c < PER; ++c) {
+            const int k = k0 + ((c * T + tid) % KCH) * 8;
+            reg[set][c] = load16_unaligned(row[c] + min(k, kmax));
+        }
+    }
+    // TAIL: the slice reaches past K (only then can a chunk need its clamp undone).
+    template <bool TAIL>
+    __device__ __forceinline__ void store_t(int set, int tid, uint16_t *lds, int k0) const {
+#pragma unroll
+        for (int c = 0; c < PER; ++c) {
+            const int q = c * T + tid;
+            if ((NCH % T == 0) || q < NCH) {
+                const int r = q / KCH, kc = q % KCH;
+                u32x4 v = reg[set][c];
+                if constexpr (TAIL) {
+                    const int k = k0 + kc * 8;
+                    v = drop_elems(v, k - min(k, kmax));
+                }
+                if (r >= rows_valid) v = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = v;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(int set, int tid, uint16_t *lds, int k0) const {
+        if (k0 + BK > kmax + 8) store_t<true>(set, tid, lds, k0);
+        else store_t<false>(set, tid, lds, k0);
+    }
+};
 
 // Writes the accumulator tile (lane l, register r of block (i, j) is element
 // (row_base + 32i + 8(r/4) + r%4, col_base + 32j)) to C, masked to C's view
@@ -879,10 +951,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
     // step kt and written to LDS at step kt+P-2, so P-1 steps of products
     // cover a load's latency. Small tiles do little work per step and take
     // 4 sets; 128x128 and larger keep 2 (their registers are the limit).
+    // Small tiles whose operands are both k-contiguous (any alignment) run
+    // the branch-free loop below (KuStream): the K tail is loaded like every
+    // other slice, 16 bytes per chunk, instead of element by element behind
+    // a branch, which made its step wait a full memory latency. (The host
+    // sends such problems here only when K >= 8.)
+    constexpr bool DEEP = LA == LD_KU && LB == LD_KU && BM * BN < 128 * 128;
     constexpr int P = BM * BN < 128 * 128 ? 4 : 2;
     // With P = 2 one set serves both roles (requested at the top of a step,
     // written at its end), as the register budget of the large tiles needs.
-    constexpr int NSET = P == 2 ? 1 : P;
+    constexpr int NSET = (P == 2 || DEEP) ? 1 : P;
     TileLoader<BM, BK, LDK, T, LA> la[NSET];
     TileLoader<BN, BK, LDK, T, LB> lb[NSET];
     const uint16_t *A = static_cast<const uint16_t *>(g.A) + (int64_t)w.prod * g.bsa;
@@ -914,9 +992,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
     // row-contiguous operand's tile has all its rows.
     const bool full_rows = (LA != LD_RU || la[0].rows_valid == BM) && (LB != LD_RU || lb[0].rows_valid == BN);
     const int n_fast = full_rows ? kl / BK : 0;
+
 #pragma unroll
     for (int p = 0; p + 1 < P; ++p) {
-        if (p < nk) {
+        if (!DEEP && p < nk) {
             if (full_rows && (p + 1) * BK <= kl) {  // p < n_fast
                 la[p % NSET].template load<true>(tid, p * BK);
                 lb[p % NSET].template load<true>(tid, p * BK);
@@ -926,7 +1005,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
             }
         }
     }
-    if (nk > 0) {
+    if (!DEEP && nk > 0) {
         la[0].store(tid, lds[0]);
         lb[0].store(tid, lds[0] + BM * LDK);
         __syncthreads();
@@ -956,7 +1035,53 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
                 for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<TI>::run(af[i], bf[j], acc[i][j]);
         }
     };
-    if constexpr (P == 2) {
+    if constexpr (DEEP) {
+        // Slices 0..P-2 into sets 0..P-2, then whole groups of P steps: step
+        // kt requests slice kt+P-1 (a clamped dummy past K) and writes slice
+        // kt+1 into the other buffer; straight-line code with compile-time
+        // set and buffer indices. The last nk - kt0 < P steps load nothing
+        // (every slice they need was requested).
+        KuStream<BM, BK, LDK, T, P> sa;
+        KuStream<BN, BK, LDK, T, P> sb;
+        sa.init(la[0].base, g.sam, la[0].rows_valid, kl, tid);
+        sb.init(lb[0].base, g.sbn, lb[0].rows_valid, kl, tid);
+#pragma unroll
+        for (int p = 0; p + 1 < P; ++p) {
+            sa.load(p, tid, p * BK);
+            sb.load(p, tid, p * BK);
+        }
+        sa.store(0, tid, lds[0], 0);
+        sb.store(0, tid, lds[0] + BM * LDK, 0);
+        __syncthreads();
+        int kt0 = 0;
+        for (; kt0 + P <= nk; kt0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) {
+                const int kt = kt0 + u;
+                sa.load((u + P - 1) % P, tid, (kt + P - 1) * BK);
+                sb.load((u + P - 1) % P, tid, (kt + P - 1) * BK);
+                multiply(u);
+                sa.store((u + 1) % P, tid, lds[(u & 1) ^ 1], (kt + 1) * BK);
+                sb.store((u + 1) % P, tid, lds[(u & 1) ^ 1] + BM * LDK, (kt + 1) * BK);
+                __syncthreads();
+                // keep each step's work in its step: moved earlier, the
+                // stores' arithmetic would wait for loads still in flight
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int kt = kt0 + u;
+            if (kt < nk) {
+                multiply(u);
+                if (kt + 1 < nk) {
+                    sa.store((u + 1) % P, tid, lds[(u & 1) ^ 1], (kt + 1) * BK);
+                    sb.store((u + 1) % P, tid, lds[(u & 1) ^ 1] + BM * LDK, (kt + 1) * BK);
+                }
+                __syncthreads();
+            }
+        }
+    } else if constexpr (P == 2) {
         // The large tiles: one register set, requested at the top of a step
         // and written at its end (their registers do not allow more). First
         // the steps whose next slice takes the branch-free loads, then the
@@ -1409,6 +1534,240 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
         step(std::true_type{}, lds + fill * STAGE, lds + cur * STAGE, lds + next * STAGE, kt);
     }
     wait_vmcnt<0>();  // the out-of-range tail loads must land before the workgroup can exit
+
+    finish_tile<EM, BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
+}
+
+// ============================================================================
+// gemm_mfma_rs: register-staged operands in the direct kernel's LDS formats
+// ============================================================================
+//
+// For contiguous operands whose rows (LD_KU) or k-lines (LD_RU) are not
+// 16-byte aligned, so the buffer unit cannot write them to LDS directly. Each
+// thread fetches, with unaligned 16-byte global loads, the chunks that a
+// direct load would have placed in its lane's LDS slots (the same KTile /
+// RTile layouts and swizzles), and writes them there before the step's
+// barrier; fragments, products and the pipeline are those of gemm_mfma_lds.
+// Every load is branch-free: rows are clamped into the operand and, past K,
+// k is clamped to the last chunk that lies inside it; the write to LDS undoes
+// the clamp (the elements read early are shifted out, chunks outside the view
+// become zeros). The host sends a problem here only when the clamps stay
+// inside the operand: K >= 8 for an LD_KU operand, and at least 8 rows (M or
+// N) for an LD_RU operand.
+template <int ROWS, int BK, int MODE, int NW, int R>
+struct StagedLoader {
+    static_assert(MODE == LD_KU || MODE == LD_RU, "contiguous operands");
+    using KT = KTile<ROWS, BK>;
+    using RT = RTile<ROWS, BK>;
+    static constexpr int NLOADS = MODE == LD_KU ? KT::NLOADS : RT::NLOADS;
+    static constexpr int PER = NLOADS / NW;
+    static_assert(NLOADS % NW == 0, "wave loads must split evenly over the waves");
+
+    u32x4 reg[R][PER];         // R register sets
+    const uint16_t *ptr[PER];  // KU: clamped row at k = 0; RU: k-line 0 at the clamped first row
+    int kmax;                  // KU: K - 8 (last chunk start); RU: K - 1 (last k-line)
+    int64_t sk;                // RU: element stride between k-lines
+    int rows_valid;
+
+    // The chunk (row, k) that wave load b puts in lane `lane`'s slot.
+    __device__ static __forceinline__ void chunk(int b, int lane, int &row, int &k) {
+        if constexpr (MODE == LD_KU) KT::src(b, lane, row, k);
+        else RT::src(b, lane, k, row);
+    }
+    // Rows the clamped load starts early (8 or more: none of its rows is valid).
+    __device__ __forceinline__ int row_shift(int row) const {
+        if constexpr (MODE == LD_KU) return row < rows_valid ? 0 : 8;
+        else return min(row - min(row, rows_valid - 8), 8);
+    }
+
+    __device__ __forceinline__ void init(const uint16_t *origin, int64_t srow, int64_t sk_, int rows, int K,
+                                         int wave, int lane) {
+        rows_valid = rows;
+        sk = sk_;
+        kmax = MODE == LD_KU ? K - 8 : K - 1;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            int row, k;
+            chunk(wave + NW * j, lane, row, k);
+            if constexpr (MODE == LD_KU) ptr[j] = origin + (int64_t)(row < rows ? row : rows - 1) * srow;
+            else ptr[j] = origin + min(row, rows - 8);  // below the tile on one of fewer than 8 rows
+        }
+    }
+
+    template <int SET>
+    __device__ __forceinline__ void load(int k0, int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            int row, kin;
+            chunk(wave + NW * j, lane, row, kin);
+            const int k = min(k0 + kin, kmax);
+            reg[SET][j] = load16_unaligned(MODE == LD_KU ? ptr[j] + k : ptr[j] + (int64_t)k * sk);
+        }
+    }
+
+    // Writes set SET (the slice loaded for k0) into `tile` (this wave's
+    // slots). CLAMP: some chunk may need its clamp undone (the slice reaches
+    // past K, or the tile has fewer valid rows than ROWS); otherwise the
+    // registers go to LDS as they are.
+    template <int SET, bool CLAMP>
+    __device__ __forceinline__ void store(char *tile, int k0, int wave, int lane) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            u32x4 v = reg[SET][j];
+            if constexpr (CLAMP) {
+                int row, kin;
+                chunk(wave + NW * j, lane, row, kin);
+                const int k = k0 + kin;
+                if constexpr (MODE == LD_KU) {
+                    v = drop_elems(v, row_shift(row) + (k - min(k, kmax)));
+                } else {
+                    v = drop_elems(v, row_shift(row));
+                    if (k > kmax) v = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            *reinterpret_cast<u32x4 *>(tile + (wave + NW * j) * 1024 + lane * 16) = v;
+        }
+    }
+
+    __device__ __forceinline__ u32x4 frag(const char *tile, int r0, int k0, int lane) const {
+        if constexpr (MODE == LD_KU) return frag_from_ktile<ROWS, BK>(tile, r0, k0, lane);
+        else return frag_from_rtile<ROWS, BK>(tile, r0, k0, lane);
+    }
+};
+
+// Register sets of the staged kernel: slice s is requested R steps before it
+// is written to LDS (R steps of products cover its latency); S = R + 1 LDS
+// stages. The 256x256x64 tile has room for one set only.
+template <int BM, int BN, int BK>
+constexpr int staged_sets() {
+    return (BM * BN >= 256 * 256 && BK >= 64) ? 1 : 2;
+}
+
+// WM x WN waves (every wave loads).
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int EM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_rs(GemmArgs g) {
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int R = staged_sets<BM, BN, BK>();
+    constexpr int S = R + 1;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+
+    const WorkItem w = work_item(blockIdx.x, g);
+    const int m0 = w.pm * BM, n0 = w.pn * BN;
+    const int k_begin = w.split * g.k_chunk;
+    const int kl = min(g.K - k_begin, g.k_chunk);  // this workgroup's K range
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    StagedLoader<BM, BK, LA, NW, R> la;
+    StagedLoader<BN, BK, LB, NW, R> lb;
+    const int rows_a = min(BM, g.M - m0), rows_b = min(BN, g.N - n0);
+    la.init(static_cast<const uint16_t *>(g.A) + (int64_t)w.prod * g.bsa + (int64_t)m0 * g.sam +
+                (int64_t)k_begin * g.sak,
+            g.sam, g.sak, rows_a, kl, wave, lane);
+    lb.init(static_cast<const uint16_t *>(g.B) + (int64_t)w.prod * g.bsb + (int64_t)n0 * g.sbn +
+                (int64_t)k_begin * g.sbk,
+            g.sbn, g.sbk, rows_b, kl, wave, lane);
+    const bool edge = rows_a < BM || rows_b < BN;  // some row clamp to undo
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = (kl + BK - 1) / BK;
+    constexpr int KSUB = BK / 16;
+    u32x4 af[2][FM], bf[2][FN];
+    auto fetch = [&](const char *stage, int kk, int set) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[set][j] = lb.frag(stage + A_BYTES, wn * WTN + j * 32, kk * 16, lane);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[set][i] = la.frag(stage, wm * WTM + i * 32, kk * 16, lane);
+    };
+    auto mfmas = [&](int set, int from, int to) {
+#pragma unroll
+        for (int t = from; t < to; ++t) acc[t / FN][t % FN] = Mfma<TI>::run(af[set][t / FN], bf[set][t % FN], acc[t / FN][t % FN]);
+    };
+    // Writes slice k0 from register set SET into `stage`.
+    auto commit = [&](auto set_tag, char *stage, int k0) {
+        constexpr int SET = decltype(set_tag)::value;
+        if (edge || k0 + BK > kl) {
+            la.template store<SET, true>(stage, k0, wave, lane);
+            lb.template store<SET, true>(stage + A_BYTES, k0, wave, lane);
+        } else {
+            la.template store<SET, false>(stage, k0, wave, lane);
+            lb.template store<SET, false>(stage + A_BYTES, k0, wave, lane);
+        }
+    };
+    auto load = [&](auto set_tag, int k0) {
+        constexpr int SET = decltype(set_tag)::value;
+        la.template load<SET>(k0, wave, lane);
+        lb.template load<SET>(k0, wave, lane);
+    };
+    if (nk > 0) {
+        load(std::integral_constant<int, 0>{}, 0);
+        if constexpr (R > 1) load(std::integral_constant<int, 1 % R>{}, BK);
+        commit(std::integral_constant<int, 0>{}, lds, 0);
+        stage_barrier();
+        fetch(lds, 0, 0);
+    }
+    constexpr int NMFMA = FM * FN;
+    constexpr int NREAD = FM * (LA == LD_KU ? 1 : 2) + FN * (LB == LD_KU ? 1 : 2);
+    constexpr int NLOAD = StagedLoader<BM, BK, LA, NW, R>::PER + StagedLoader<BN, BK, LB, NW, R>::PER;
+    static_assert(KSUB % 2 == 0, "substep 0 of every slice uses fragment set 0");
+    // Step kt over slice kt in stage `cur`: request slice kt+R into set kt%R
+    // (a clamped dummy past K; the set's previous slice, kt, went to LDS in
+    // the previous step), multiply, write slice kt+1 (set (kt+1)%R) into
+    // stage `next` (last read R steps ago), synchronise, fetch the first
+    // fragments of slice kt+1.
+    auto step = [&](auto u_tag, char *__restrict__ cur, char *next, int kt) {
+        constexpr int U = decltype(u_tag)::value;  // kt % R
+        load(std::integral_constant<int, U>{}, (kt + R) * BK);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KSUB; ++kk) {
+            fetch(cur, kk + 1, (kk & 1) ^ 1);
+            mfmas(kk & 1, 0, NMFMA);
+        }
+        constexpr int LAST = (KSUB - 1) & 1;
+        mfmas(LAST, 0, NMFMA / 2);
+        // the loads go out with the first substep's products
+        interleave_mfma<NMFMA, NREAD, NLOAD>();
+        interleave_mfma<NMFMA * (KSUB - 2), NREAD * (KSUB - 2), 0>();
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA / 2, 0);
+        sched_fence();
+        commit(std::integral_constant<int, (U + 1) % R>{}, next, (kt + 1) * BK);
+        stage_barrier();
+        sched_fence();
+        fetch(next, 0, LAST ^ 1);
+        mfmas(LAST, NMFMA / 2, NMFMA);
+        interleave_mfma<NMFMA - NMFMA / 2, NREAD, 0>();
+        sched_fence();
+    };
+    // R steps per iteration so the register set is a compile-time index; the
+    // stages rotate at run time (slice kt lives in stage kt % S).
+    int kt = 0, cur = 0;
+    auto stage_at = [&](int s) { return lds + s * STAGE; };
+    auto advance = [&](int c) { return c + 1 == S ? 0 : c + 1; };
+    for (; kt + R <= nk; kt += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int nx = advance(cur);
+            if (u == 0) step(std::integral_constant<int, 0>{}, stage_at(cur), stage_at(nx), kt);
+            else step(std::integral_constant<int, 1 % R>{}, stage_at(cur), stage_at(nx), kt + 1);
+            cur = nx;
+        }
+    }
+    if (kt < nk) {  // R = 2 and one step left
+        step(std::integral_constant<int, 0>{}, stage_at(cur), stage_at(advance(cur)), kt);
+    }
 
     finish_tile<EM, BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
 }

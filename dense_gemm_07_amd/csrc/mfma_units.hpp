@@ -12,12 +12,23 @@ constexpr bool direct_to_lds() {
     return (LA == LD_KC || LA == LD_RC) && (LB == LD_KC || LB == LD_RC);
 }
 
+// Large tiles with contiguous (but not 16-byte aligned) operands stage them
+// through registers into the direct kernel's LDS formats; small tiles and
+// element-wise (LD_GN) operands keep the padded-row register kernel.
+template <int BM, int BN, int LA, int LB>
+constexpr bool staged_direct_format() {
+    return BM * BN >= 128 * 128 && (LA == LD_KU || LA == LD_RU) && (LB == LD_KU || LB == LD_RU);
+}
+
 template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S, int EM>
 void launch_mode(const GemmArgs &g, hipStream_t s) {
     const unsigned groups = launch_groups(g);
     if constexpr (direct_to_lds<LA, LB>())
         hipLaunchKernelGGL((gemm_mfma_lds<TI, BM, BN, BK, WM, WN, LA, LB, S, EM>), dim3(groups), dim3(WM * WN * 64),
                            0, s, g);
+    else if constexpr (staged_direct_format<BM, BN, LA, LB>())
+        hipLaunchKernelGGL((gemm_mfma_rs<TI, BM, BN, BK, WM, WN, LA, LB, EM>), dim3(groups), dim3(WM * WN * 64), 0,
+                           s, g);
     else
         hipLaunchKernelGGL((gemm_mfma<TI, BM, BN, BK, WM, WN, LA, LB, EM>), dim3(groups), dim3(WM * WN * 64), 0, s, g);
 }
@@ -36,7 +47,9 @@ template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, i
 void add_mfma(std::vector<KernelEntry> &out) {
     out.push_back(KernelEntry{dg_config{BM, BN, BK, 1, WM * WN, S, DG_VARIANT_MFMA, 0, 1}, TI::code, -1, LA, LB,
                               &launch_mfma<TI, BM, BN, BK, WM, WN, LA, LB, S>,
-                              direct_to_lds<LA, LB>() ? "gemm_mfma_lds" : "gemm_mfma"});
+                              direct_to_lds<LA, LB>()                   ? "gemm_mfma_lds"
+                              : staged_direct_format<BM, BN, LA, LB>() ? "gemm_mfma_rs"
+                                                                         : "gemm_mfma"});
 }
 
 // Every tile shape has a two-stage kernel for every load-mode pair (the

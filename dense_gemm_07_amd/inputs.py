@@ -74,6 +74,11 @@ EXTRA = {
         Workload("splitk_512x512x16384_bf16", 512, 512, 16384, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
         Workload("splitk_128x4096x8192_bf16", 128, 4096, 8192, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
         Workload("splitk_256x256x32768_bf16", 256, 256, 32768, "bf16", "f32", ("normal", 0.02), ("normal", 0.02)),
+        Workload("splitk_2048x512x8192_bf16", 2048, 512, 8192, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
+        Workload("splitk_512x512x4096_bf16", 512, 512, 4096, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
+        Workload("splitk_128x128x8192_bf16", 128, 128, 8192, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
+        Workload("splitk_64x64x65536_bf16", 64, 64, 65536, "bf16", "f32", ("normal", 0.02), ("normal", 0.02)),
+        Workload("square_1024_bf16", 1024, 1024, 1024, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
         Workload("bmm_1024x1024x128_bf16", 1024, 1024, 128, "bf16", "bf16", ("normal", 1.0), ("normal", 1.0)),
     ]
 }

@@ -166,6 +166,72 @@ def test_split_k_deterministic_and_workspace_needs_no_init():
     assert_within_tol(got, ref, epilogue_tolerance(K, "bf16", "bf16", got, ref, 1.0, np.abs(ref), "none"), "split")
 
 
+@pytest.mark.parametrize("K", [8, 9, 15, 40, 63, 65, 129, 448, 449, 512, 513, 777, 1029])
+def test_k_contiguous_unaligned_small_tiles_bit_exact(K):
+    """Both operands k-contiguous at leading dimensions that are not multiples
+    of 8 and bases off 16-byte alignment: the small tiles' deep pipeline, whose
+    every chunk is a 16-byte load clamped into the row (the chunk cut by K is
+    read from K - 8 and shifted into place). K spans one slice, the group of
+    eight steps, ragged tails, and split-K ranges down to 5 elements
+    (K = 1029 cut for 16 ranges: 9 ranges of 128, the last of 5). Integers, bit-exact."""
+    M, N = 130, 70
+    a, b = inputs.integer_operands(M, N, K, "bf16", seed=K + 7)
+    big_a = torch.zeros((M, K + 3), dtype=torch.bfloat16)
+    big_a[:, 1:K + 1] = a
+    big_b = torch.zeros((N, K + 1), dtype=torch.bfloat16)  # B's storage, one row per column of B
+    big_b[:, :K] = b.t()
+    a_dev = big_a.to(DEV)[:, 1:K + 1]                       # lda = K + 3, base 2 bytes past alignment
+    b_dev = big_b.to(DEV)[:, :K].t()                        # B[k][n] at n * (K + 1) + k
+    want32 = ref_product(a, b, "bf16")
+    for cfg_shape, splits in [((64, 64, 64, 4), 1), ((64, 64, 32, 8), 1), ((64, 64, 64, 4), 16),
+                              ((64, 64, 32, 2), 3)]:
+        cfg = config("bf16", *cfg_shape, splits=splits)
+        for out_dtype in ("f32", "bf16"):
+            what = f"K={K} cfg={cfg_shape} splits={splits} -> {out_dtype}"
+            note(what)
+            c = dg.gemm_ex(a_dev, b_dev, out_dtype=TD[out_dtype], config=cfg)
+            torch.cuda.synchronize()
+            assert_bits_equal(out_bits(c, out_dtype), oracle.encode(want32, out_dtype), what)
+
+
+def _offset_view(t, colmajor, pad):
+    """Device view of CPU matrix t [rows, cols]: row-major (or column-major)
+    storage whose leading dimension is `pad` elements wider than needed and
+    whose base sits one element past a 16-byte boundary."""
+    store = t.t() if colmajor else t
+    r, c = store.shape
+    big = torch.zeros((r, c + pad), dtype=t.dtype)
+    big[:, 1:c + 1] = store
+    v = big.to(DEV)[:, 1:c + 1]
+    return v.t() if colmajor else v
+
+
+@pytest.mark.parametrize("shape", [(257, 263, 777), (300, 9, 520), (9, 300, 100), (515, 130, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_staged_large_tiles_bit_exact(shape):
+    """Large tiles with contiguous operands off 16-byte alignment: registers
+    stage them into the direct kernel's LDS formats. Each operand k-contiguous
+    or row-contiguous; edge tiles with fewer than 8 valid rows, K tails that
+    are not multiples of 8, products of less than one tile. Integers,
+    bit-exact."""
+    M, N, K = shape
+    a, b = inputs.integer_operands(M, N, K, "bf16", seed=M + 3 * N + 7 * K)
+    want32 = ref_product(a, b, "bf16")
+    for a_col in (False, True):
+        for b_col in (False, True):
+            ad = _offset_view(a, a_col, 3)
+            bd = _offset_view(b, b_col, 5)
+            for cfg_shape in [(256, 256, 64, 2), (256, 256, 32, 2), (128, 128, 64, 2), (256, 128, 64, 2),
+                              (128, 256, 64, 2)]:
+                cfg = config("bf16", *cfg_shape)
+                for out_dtype in ("f32", "bf16"):
+                    what = f"{shape} A {'col' if a_col else 'row'} B {'col' if b_col else 'row'} {cfg_shape} -> {out_dtype}"
+                    note(what)
+                    c = dg.gemm_ex(ad, bd, out_dtype=TD[out_dtype], config=cfg)
+                    torch.cuda.synchronize()
+                    assert_bits_equal(out_bits(c, out_dtype), oracle.encode(want32, out_dtype), what)
+
+
 def test_split_k_workspace_per_stream():
     """The binding's cached workspace is one buffer per (device, stream): split-K
     calls queued on two streams at once write their partial tiles into
