@@ -1640,7 +1640,7 @@ struct StagedLoader {
 // stages. The 256x256x64 tile has room for one set only.
 template <int BM, int BN, int BK>
 constexpr int staged_sets() {
-    return (BM * BN >= 256 * 256 && BK >= 64) ? 1 : 2;
+    return (BM * BN >= 256 * 256 && BK >= 64) ? 1 : (BM * BN >= 128 * 128 ? 2 : 3);
 }
 
 // WM x WN waves (every wave loads).
@@ -1713,8 +1713,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_rs(GemmArgs g) {
         lb.template load<SET>(k0, wave, lane);
     };
     if (nk > 0) {
+        // slices 0..R-1 into sets 0..R-1
         load(std::integral_constant<int, 0>{}, 0);
         if constexpr (R > 1) load(std::integral_constant<int, 1 % R>{}, BK);
+        if constexpr (R > 2) load(std::integral_constant<int, 2 % R>{}, 2 * BK);
         commit(std::integral_constant<int, 0>{}, lds, 0);
         stage_barrier();
         fetch(lds, 0, 0);
@@ -1753,21 +1755,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_rs(GemmArgs g) {
     };
     // R steps per iteration so the register set is a compile-time index; the
     // stages rotate at run time (slice kt lives in stage kt % S).
+    static_assert(R >= 1 && R <= 3, "register sets");
     int kt = 0, cur = 0;
-    auto stage_at = [&](int s) { return lds + s * STAGE; };
-    auto advance = [&](int c) { return c + 1 == S ? 0 : c + 1; };
+    auto step_u = [&](auto u_tag, int k) {
+        const int nx = cur + 1 == S ? 0 : cur + 1;
+        step(u_tag, lds + cur * STAGE, lds + nx * STAGE, k);
+        cur = nx;
+    };
     for (; kt + R <= nk; kt += R) {
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const int nx = advance(cur);
-            if (u == 0) step(std::integral_constant<int, 0>{}, stage_at(cur), stage_at(nx), kt);
-            else step(std::integral_constant<int, 1 % R>{}, stage_at(cur), stage_at(nx), kt + 1);
-            cur = nx;
-        }
+        step_u(std::integral_constant<int, 0>{}, kt);
+        if constexpr (R > 1) step_u(std::integral_constant<int, 1 % R>{}, kt + 1);
+        if constexpr (R > 2) step_u(std::integral_constant<int, 2 % R>{}, kt + 2);
     }
-    if (kt < nk) {  // R = 2 and one step left
-        step(std::integral_constant<int, 0>{}, stage_at(cur), stage_at(advance(cur)), kt);
-    }
+    // fewer than R steps left; their register sets are 0, 1, ...
+    if (kt < nk) step_u(std::integral_constant<int, 0>{}, kt);
+    if constexpr (R > 2)
+        if (kt + 1 < nk) step_u(std::integral_constant<int, 1 % R>{}, kt + 1);
 
     finish_tile<EM, BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
 }

@@ -14,7 +14,10 @@ constexpr bool direct_to_lds() {
 
 // Large tiles with contiguous (but not 16-byte aligned) operands stage them
 // through registers into the direct kernel's LDS formats; small tiles and
-// element-wise (LD_GN) operands keep the padded-row register kernel.
+// element-wise (LD_GN) operands keep the padded-row register kernel (for the
+// 64x64 tiles of a 1000x1500x777 product the staged format measured 10 %
+// slower: their short steps are bound by per-step costs, not by the LDS
+// format).
 template <int BM, int BN, int LA, int LB>
 constexpr bool staged_direct_format() {
     return BM * BN >= 128 * 128 && (LA == LD_KU || LA == LD_RU) && (LB == LD_KU || LB == LD_RU);
