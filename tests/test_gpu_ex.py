@@ -101,6 +101,12 @@ def test_split_k_integers_bit_exact(shape, splits):
             for la, lb in LAYOUTS:
                 what = f"{shape} splits={splits} cfg={cfg_shape} {la}/{lb} -> {out_dtype}"
                 note(what)
+                if la == "gap" and cfg_shape[:3] == (256, 256, 64):
+                    # element-load operands have no 256x256x64 kernel (it would spill)
+                    with pytest.raises(dg.DGError) as e:
+                        dg.gemm_ex(place(a, la), place(b, lb), out_dtype=TD[out_dtype], config=cfg)
+                    assert e.value.status == 3, what
+                    continue
                 c = dg.gemm_ex(place(a, la), place(b, lb), out_dtype=TD[out_dtype], config=cfg)
                 torch.cuda.synchronize()
                 assert_bits_equal(out_bits(c, out_dtype), want, what)
