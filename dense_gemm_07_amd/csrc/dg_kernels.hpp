@@ -1550,10 +1550,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
 // barrier; fragments, products and the pipeline are those of gemm_mfma_lds.
 // Every load is branch-free: rows are clamped into the operand and, past K,
 // k is clamped to the last chunk that lies inside it; the write to LDS undoes
-// the clamp (the elements read early are shifted out, chunks outside the view
-// become zeros). The host sends a problem here only when the clamps stay
-// inside the operand: K >= 8 for an LD_KU operand, and at least 8 rows (M or
-// N) for an LD_RU operand.
+// the clamp (the elements read early are shifted out, k past K becomes zeros;
+// a k-contiguous operand's rows past the valid ones keep the clamped row,
+// which only feeds accumulators outside C's view). The host sends a problem
+// here only when the clamps stay inside the operand: K >= 8 for an LD_KU
+// operand, and at least 8 rows (M or N) for an LD_RU operand.
 template <int ROWS, int BK, int MODE, int NW, int R>
 struct StagedLoader {
     static_assert(MODE == LD_KU || MODE == LD_RU, "contiguous operands");
@@ -1564,9 +1565,9 @@ struct StagedLoader {
     static_assert(NLOADS % NW == 0, "wave loads must split evenly over the waves");
 
     u32x4 reg[R][PER];         // R register sets
-    const uint16_t *ptr[PER];  // KU: clamped row at k = 0; RU: k-line 0 at the clamped first row
+    const uint16_t *origin;    // element (tile row 0, k = 0) of the operand
+    int64_t srow, sk;          // element strides along rows and along k
     int kmax;                  // KU: K - 8 (last chunk start); RU: K - 1 (last k-line)
-    int64_t sk;                // RU: element stride between k-lines
     int rows_valid;
 
     // The chunk (row, k) that wave load b puts in lane `lane`'s slot.
@@ -1574,26 +1575,20 @@ struct StagedLoader {
         if constexpr (MODE == LD_KU) KT::src(b, lane, row, k);
         else RT::src(b, lane, k, row);
     }
-    // Rows the clamped load starts early (8 or more: none of its rows is valid).
-    __device__ __forceinline__ int row_shift(int row) const {
-        if constexpr (MODE == LD_KU) return row < rows_valid ? 0 : 8;
-        else return min(row - min(row, rows_valid - 8), 8);
-    }
+    // LD_RU: rows the clamped load starts early (8 or more: none of its rows is valid).
+    __device__ __forceinline__ int row_shift(int row) const { return min(row - min(row, rows_valid - 8), 8); }
 
-    __device__ __forceinline__ void init(const uint16_t *origin, int64_t srow, int64_t sk_, int rows, int K,
-                                         int wave, int lane) {
-        rows_valid = rows;
+    __device__ __forceinline__ void init(const uint16_t *origin_, int64_t srow_, int64_t sk_, int rows, int K) {
+        origin = origin_;
+        srow = srow_;
         sk = sk_;
+        rows_valid = rows;
         kmax = MODE == LD_KU ? K - 8 : K - 1;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            int row, k;
-            chunk(wave + NW * j, lane, row, k);
-            if constexpr (MODE == LD_KU) ptr[j] = origin + (int64_t)(row < rows ? row : rows - 1) * srow;
-            else ptr[j] = origin + min(row, rows - 8);  // below the tile on one of fewer than 8 rows
-        }
     }
 
+    // Chunk addresses are recomputed per slice from the uniform origin and
+    // strides (a few integer operations) rather than kept per chunk: the
+    // 256x256 tile has no registers to spare.
     template <int SET>
     __device__ __forceinline__ void load(int k0, int wave, int lane) {
 #pragma unroll
@@ -1601,7 +1596,13 @@ struct StagedLoader {
             int row, kin;
             chunk(wave + NW * j, lane, row, kin);
             const int k = min(k0 + kin, kmax);
-            reg[SET][j] = load16_unaligned(MODE == LD_KU ? ptr[j] + k : ptr[j] + (int64_t)k * sk);
+            if constexpr (MODE == LD_KU) {
+                const int rc = row < rows_valid ? row : rows_valid - 1;
+                reg[SET][j] = load16_unaligned(origin + (int64_t)rc * srow + k);
+            } else {
+                const int rc = min(row, rows_valid - 8);  // below the tile on one of fewer than 8 rows
+                reg[SET][j] = load16_unaligned(origin + rc + (int64_t)k * sk);
+            }
         }
     }
 
@@ -1619,7 +1620,10 @@ struct StagedLoader {
                 chunk(wave + NW * j, lane, row, kin);
                 const int k = k0 + kin;
                 if constexpr (MODE == LD_KU) {
-                    v = drop_elems(v, row_shift(row) + (k - min(k, kmax)));
+                    // rows past the valid ones keep the clamped row's data:
+                    // they only reach accumulators of C rows (or columns)
+                    // outside the view, which are never stored
+                    v = drop_elems(v, k - min(k, kmax));
                 } else {
                     v = drop_elems(v, row_shift(row));
                     if (k > kmax) v = u32x4{0u, 0u, 0u, 0u};
@@ -1669,11 +1673,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_rs(GemmArgs g) {
     const int rows_a = min(BM, g.M - m0), rows_b = min(BN, g.N - n0);
     la.init(static_cast<const uint16_t *>(g.A) + (int64_t)w.prod * g.bsa + (int64_t)m0 * g.sam +
                 (int64_t)k_begin * g.sak,
-            g.sam, g.sak, rows_a, kl, wave, lane);
+            g.sam, g.sak, rows_a, kl);
     lb.init(static_cast<const uint16_t *>(g.B) + (int64_t)w.prod * g.bsb + (int64_t)n0 * g.sbn +
                 (int64_t)k_begin * g.sbk,
-            g.sbn, g.sbk, rows_b, kl, wave, lane);
-    const bool edge = rows_a < BM || rows_b < BN;  // some row clamp to undo
+            g.sbn, g.sbk, rows_b, kl);
+    const bool edge = (LA == LD_RU && rows_a < BM) || (LB == LD_RU && rows_b < BN);  // an RU row clamp to undo
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -1701,6 +1705,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_rs(GemmArgs g) {
         constexpr int SET = decltype(set_tag)::value;
         if (edge || k0 + BK > kl) {
             la.template store<SET, true>(stage, k0, wave, lane);
+            sched_fence();  // one operand's shifts at a time (registers)
             lb.template store<SET, true>(stage + A_BYTES, k0, wave, lane);
         } else {
             la.template store<SET, false>(stage, k0, wave, lane);
