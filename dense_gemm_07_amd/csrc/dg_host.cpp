@@ -435,15 +435,12 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
     best.k_splits = 1;
     // Split-K (measured on MI355X, 64x64 tiles): S ranges pay when the tiles
     // leave CUs idle and each range keeps >= 1024 of K, so S = CUs / tiles,
-    // capped by K / 1024 and 16; with K >= 8192 two ranges pay even when the
-    // tiles just fill the CUs, if two workgroups fit per CU (LDS of 160 KiB
-    // per CU). Below that the second kernel and the partial-tile traffic cost
-    // more than they save.
+    // capped by K / 1024 and 16. When the tiles fill the CUs the second
+    // kernel and the partial-tile traffic cost more than they save (even at
+    // K = 8192: 2048x512x8192 takes 29.8 us unsplit, 32.4 us at S = 2).
     if (best.variant == DG_VARIANT_MFMA && ws_bytes > 0 && p.K > 0) {
         const int64_t tiles = ((p.M + best.block_m - 1) / best.block_m) * ((p.N + best.block_n - 1) / best.block_n) * nb;
         int64_t s = (int64_t)cus / std::max<int64_t>(tiles, 1);
-        const int64_t lds = (int64_t)best.stages * (best.block_m + best.block_n) * best.block_k * 2;
-        if (p.K >= 8192 && tiles <= cus && 2 * lds <= 160 * 1024) s = std::max<int64_t>(s, 2);
         s = std::min<int64_t>({s, 16, p.K / 1024});
         if (s >= 2) {
             dg_config c = best;

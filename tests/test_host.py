@@ -327,7 +327,7 @@ def test_autotune_ex_rejects_epilogue_reading_c():
 def test_gemm_ex_default_split_choice():
     """Split counts the library picks for dg_gemm_ex with a workspace (the measured rule)."""
     cases = {(1024, 1024, 1024): 1, (1, 14336, 4096): 1, (512, 512, 4096): 4, (256, 256, 32768): 16,
-             (2048, 512, 8192): 2, (128, 128, 8192): 8, (64, 64, 65536): 16}
+             (2048, 512, 8192): 1, (128, 4096, 8192): 2, (512, 512, 16384): 4, (128, 128, 8192): 8, (64, 64, 65536): 16}
     for (M, N, K), want in cases.items():
         c, _ = dg.select_config_ex(M, N, K, (K, 1), (N, 1), (N, 1), BF16, BF16, batch=1,
                                    workspace_bytes=1 << 30)
