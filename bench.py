@@ -280,7 +280,7 @@ def main():
                     help="time dg_gemm_ex with a workspace (the library may split K)")
     ap.add_argument("--config", default="",
                     help="time an explicit kernel config BMxBNxBK:waves:stages:group_m:xcd_remap[:k_splits] "
-                         "(ablations; k_splits > 1 with --split-k)")
+                         "(ablations; k_splits > 1, or sk for stream-K, with --split-k)")
     ap.add_argument("--misalign-a", action="store_true",
                     help="view A one element past a 16-byte boundary (forces the register-staged kernel)")
     ap.add_argument("--rotate", type=int, default=1, metavar="SETS",
@@ -378,9 +378,9 @@ def main():
         if explicit is None:
             raise SystemExit(f"no compiled kernel {args.config}")
         explicit.group_m, explicit.xcd_remap = int(group_m), int(xcd)
-        explicit.k_splits = int(more[0]) if more else 1
-        if explicit.k_splits > 1 and not args.split_k:
-            raise SystemExit("a config with k_splits > 1 needs --split-k (the workspace)")
+        explicit.k_splits = (dg.STREAM_K if more[0] == "sk" else int(more[0])) if more else 1
+        if (explicit.k_splits > 1 or explicit.k_splits == dg.STREAM_K) and not args.split_k:
+            raise SystemExit("a config with k_splits > 1 or sk needs --split-k (the workspace)")
     if explicit is not None:
         cfg = explicit
     elif ex:

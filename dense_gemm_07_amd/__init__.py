@@ -294,6 +294,7 @@ def cache_load(path):
 # out again only to later work on the same stream, which runs after every
 # kernel already queued there that reads it.
 DEFAULT_WORKSPACE_BYTES = 64 << 20
+STREAM_K = -1  # DG_STREAM_K of include/dg.h: Config.k_splits for stream-K
 NOALLOC_SCRATCH_BYTES = 32 << 20  # DG_NOALLOC_SCRATCH_BYTES of include/dg.h
 _workspaces = {}
 
@@ -314,7 +315,8 @@ def _workspace(t, nbytes, stream):
 
 
 def workspace_size(M, N, K, batch, config):
-    """Bytes of split-K workspace a config needs (0 if it does not split K)."""
+    """Bytes of workspace a config needs: split-K partials, or stream-K flags and
+    partials (0 if it needs none)."""
     total = _i64()
     _check(library().dg_workspace_size(M, N, K, batch, ctypes.byref(config), ctypes.byref(total)))
     return total.value
@@ -397,9 +399,10 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
     shared by the batch); out: [M, N] or [batch, M, N]. residual: None (R is
     out's prior contents when beta != 0) or [M, N] / [batch, M, N]. bias: [N]
     (or [M] with bias_per_row) / [batch, N]. activation: None, "relu", "gelu".
-    config: explicit Config (k_splits > 1 = split-K) or None for the library's
-    choice. workspace: True = the binding's cached split-K workspace, a CUDA
-    tensor of any dtype, or None/False for none.
+    config: explicit Config (k_splits > 1 = split-K, STREAM_K = stream-K) or
+    None for the library's choice. workspace: True = the binding's cached
+    workspace (grown to what the config needs), a CUDA tensor of any dtype,
+    or None/False for none.
     """
     out = _ex_out(a, b, out, out_dtype)
     prob, epi, batch = _ex_args(a, b, out, alpha, beta, residual, bias, bias_per_row, activation)
@@ -407,7 +410,7 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
     raw = _stream(a, stream)
     if workspace is True:
         need = 0
-        if config is not None and config.k_splits > 1:
+        if config is not None and (config.k_splits > 1 or config.k_splits == STREAM_K):
             need = workspace_size(prob[0], prob[1], prob[2], batch.count, config)
         ws = _workspace(a, need, raw)
         ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
@@ -420,7 +423,7 @@ def gemm_ex(a, b, out=None, out_dtype=None, *, alpha=1.0, beta=0.0, residual=Non
 
 def gemm_ex_noalloc(a, b, out, *, alpha=1.0, beta=0.0, residual=None, bias=None, bias_per_row=False,
                     activation=None, config=None, stream=None):
-    """dg_gemm_ex_noalloc: gemm_ex with split-K partials in the library's fixed
+    """dg_gemm_ex_noalloc: gemm_ex with split-K / stream-K partials in the library's fixed
     per-GPU scratch (NOALLOC_SCRATCH_BYTES), so neither the library nor this
     call allocates device memory; `out` must be given. Calls that overlap in
     time on one GPU share the scratch and race."""

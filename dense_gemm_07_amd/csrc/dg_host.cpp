@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cinttypes>
 #include <cstdarg>
@@ -392,6 +394,56 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t batch, const dg_config &cfg, in
     return {(int64_t)total};
 }
 
+// ---- stream-K plan -----------------------------------------------------------
+
+// One workgroup per CU (every rank resident at once), at most two per tile.
+// The ranks share out the K steps of the last, partial round of G tiles
+// together with one whole round before it, so each rank takes between one and
+// two tiles' steps and a tile is cut into at most three pieces (its owner
+// reads at most two partials); with fewer tiles than CUs, all of them.
+struct SkPlan {
+    int groups, tiles, iters, base, extra;
+};
+
+int sk_groups() { return device_info().cus; }
+
+// Stream-K workspace: the flags, then one partial tile per rank (sized for
+// one rank per CU).
+WsLayout sk_layout(int64_t M, int64_t N, int64_t batch, const dg_config &cfg) {
+    if (M == 0 || N == 0 || batch == 0) return {0};
+    const int G = sk_groups();
+    return {sk_flag_bytes(G) + (int64_t)G * cfg.block_m * cfg.block_n * 4};
+}
+
+// Workspace a config needs for a problem (0: none).
+WsLayout ws_need(int64_t M, int64_t N, int64_t K, int64_t batch, const dg_config &cfg) {
+    if (cfg.k_splits == DG_STREAM_K) return sk_layout(M, N, batch, cfg);
+    return ws_layout(M, N, batch, cfg, split_plan(K, cfg).splits);
+}
+
+// false: the shared K steps do not fit in int32 (the kernel's step numbers).
+bool sk_plan(int64_t total_tiles, int64_t K, const dg_config &cfg, SkPlan &out) {
+    const int G = (int)std::max<int64_t>(1, std::min<int64_t>(sk_groups(), 2 * total_tiles));
+    const int64_t iters = (K + cfg.block_k - 1) / cfg.block_k;
+    const int64_t rem = total_tiles % G;
+    int64_t shared = total_tiles <= G ? total_tiles : (rem == 0 ? 0 : rem + G);
+    if (iters == 0) shared = 0;
+    const int64_t S = shared * iters;
+    if (S >= ((int64_t)1 << 31) || iters >= ((int64_t)1 << 31)) return false;
+    out = SkPlan{G, (int)shared, (int)iters, (int)(S / G), (int)(S % G)};
+    return true;
+}
+
+// Launch epochs: a stream-K flag reads as raised only with this launch's
+// value. Starts at a per-process value, never 0.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> epoch{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() |
+                                       1u};
+    uint32_t e = epoch.fetch_add(1) + 1;
+    if (e == 0) e = epoch.fetch_add(1) + 1;
+    return e;
+}
+
 dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
     const auto shapes = kernel_shapes(p.in, p.out);
     const int64_t nb = p.batch < 1 ? 1 : p.batch;
@@ -449,6 +501,10 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
             if (L.total >= 0 && L.total <= ws_bytes) best = c;
         }
     }
+    // Stream-K is never the default: measured on MI355X it was slower than
+    // the unsplit kernel on every shape tried (partial last rounds of 64x64
+    // and 128x128 tiles, 1.06 to 2.25 rounds, K 777 to 4096). dg_autotune_ex
+    // times it when given a workspace.
     return best;
 }
 
@@ -497,16 +553,31 @@ dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream, voi
     if (cfg.group_m < 1) return fail(DG_ERR_NO_CONFIG, "config group_m must be >= 1");
     if (cfg.k_splits > 1 && cfg.variant != DG_VARIANT_MFMA)
         return fail(DG_ERR_NO_CONFIG, "split-K (k_splits %d) needs an MFMA config", cfg.k_splits);
+    const bool sk = cfg.k_splits == DG_STREAM_K;
+    if (sk && cfg.variant != DG_VARIANT_MFMA) return fail(DG_ERR_NO_CONFIG, "stream-K needs an MFMA config");
     const KernelEntry *e = find_kernel(cfg, p);
     if (!e)
         return fail(DG_ERR_NO_CONFIG,
                     "no compiled kernel for block %dx%dx%d waves %d stages %d variant %d with %s -> %s inputs",
                     cfg.block_m, cfg.block_n, cfg.block_k, cfg.waves, cfg.stages, cfg.variant, dtype_name(p.in),
                     dtype_name(p.out));
+    if (sk && !e->stream_k)
+        return fail(DG_ERR_NO_CONFIG, "block %dx%dx%d with %d stages has no stream-K kernel", cfg.block_m,
+                    cfg.block_n, cfg.block_k, cfg.stages);
     const int64_t gm = (p.M + cfg.block_m - 1) / cfg.block_m;
     const int64_t gn = (p.N + cfg.block_n - 1) / cfg.block_n;
     const int64_t threads = (int64_t)cfg.waves * 64;
     const SplitPlan sp = split_plan(p.K, cfg);
+    SkPlan skp{};
+    if (sk) {
+        if (gm * gn * p.batch >= ((int64_t)1 << 31) || !sk_plan(gm * gn * p.batch, p.K, cfg, skp))
+            return fail(DG_ERR_UNSUPPORTED, "too many tiles or K steps for stream-K");
+        const WsLayout L = sk_layout(p.M, p.N, p.batch, cfg);
+        if (!ws || ws_bytes < L.total)
+            return fail(DG_ERR_INVALID_VALUE, "stream-K needs a workspace of %" PRId64 " bytes (given %" PRId64 ")",
+                        L.total, ws ? ws_bytes : (int64_t)0);
+        if ((uintptr_t)ws % 256) return fail(DG_ERR_INVALID_VALUE, "workspace not 256-byte aligned");
+    }
     const int64_t per_product = gm * gn * sp.splits;  // workgroups
     const int64_t max_groups = std::min<int64_t>(((int64_t)1 << 31) - 1, (((int64_t)1 << 32) - 1) / threads);
     if (gm * gn >= ((int64_t)1 << 31) || per_product > max_groups)
@@ -540,6 +611,15 @@ dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream, voi
     g.bsa = p.bsa;
     g.bsb = p.bsb;
     g.bsc = p.bsc;
+    if (sk) {
+        g.ws = static_cast<float *>(ws);
+        g.sk_groups = skp.groups;
+        g.sk_tiles = skp.tiles;
+        g.sk_iters = skp.iters;
+        g.sk_base = skp.base;
+        g.sk_extra = skp.extra;
+        g.sk_epoch = next_epoch();
+    }
     LaunchFn reduce = nullptr;
     if (sp.splits > 1) {
         g.ws = static_cast<float *>(ws);
@@ -563,7 +643,7 @@ dg_status launch(const Problem &p, const dg_config &cfg, hipStream_t stream, voi
     g.bias_per_row = ep.per_row;
     // Products per launch: the workgroup count of one launch stays below
     // 2^31 and its thread count below 2^32.
-    const int64_t chunk = max_groups / per_product;
+    const int64_t chunk = sk ? p.batch : max_groups / per_product;  // stream-K: one launch of G ranks
     const int ie = elem_size(p.in), oe = elem_size(p.out);
     for (int64_t b0 = 0; b0 < p.batch; b0 += chunk) {
         g.batch = (int32_t)std::min<int64_t>(chunk, p.batch - b0);
@@ -647,8 +727,8 @@ dg_config choose(const Problem &p, int64_t ws_bytes, bool *from_cache = nullptr)
     dg_config c;
     const bool hit = cache_get(key_of(p), c);
     if (hit) {
-        if (c.k_splits > 1) {
-            const WsLayout L = ws_layout(p.M, p.N, p.batch, c, split_plan(p.K, c).splits);
+        if (c.k_splits > 1 || c.k_splits == DG_STREAM_K) {
+            const WsLayout L = ws_need(p.M, p.N, p.K, p.batch, c);
             if (L.total < 0 || L.total > ws_bytes) c.k_splits = 1;
         }
     } else {
@@ -814,13 +894,13 @@ dg_status dg_gemm_ex_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int
     if (p.M == 0 || p.N == 0 || p.batch == 0) return DG_OK;
     const int64_t cap = DG_NOALLOC_SCRATCH_BYTES;
     const dg_config c = cfg ? *cfg : choose(p, cap);
-    if (c.k_splits > 1) {
-        const WsLayout L = ws_layout(p.M, p.N, p.batch, c, split_plan(p.K, c).splits);
+    if (c.k_splits > 1 || c.k_splits == DG_STREAM_K) {
+        const WsLayout L = ws_need(p.M, p.N, p.K, p.batch, c);
         if (L.total < 0 || L.total > cap)
             return fail(DG_ERR_UNSUPPORTED,
-                        "split-K partials of this call need %" PRId64 " bytes of scratch; the allocation-free "
+                        "%s partials of this call need %" PRId64 " bytes of scratch; the allocation-free "
                         "entry point holds at most %" PRId64 " bytes",
-                        L.total, cap);
+                        c.k_splits == DG_STREAM_K ? "stream-K" : "split-K", L.total, cap);
     }
     void *ws = nullptr;
     s = scratch_address(&ws);
@@ -902,7 +982,7 @@ dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count
     if (M < 0 || N < 0 || K < 0 || batch_count < 0) return fail(DG_ERR_INVALID_VALUE, "negative size");
     if (cfg->block_m <= 0 || cfg->block_n <= 0 || cfg->block_k <= 0)
         return fail(DG_ERR_INVALID_VALUE, "non-positive block size");
-    const WsLayout L = ws_layout(M, N, batch_count, *cfg, split_plan(K, *cfg).splits);
+    const WsLayout L = ws_need(M, N, K, batch_count, *cfg);
     if (L.total < 0) return fail(DG_ERR_UNSUPPORTED, "workspace size overflows");
     *bytes = L.total;
     return DG_OK;
@@ -1034,7 +1114,7 @@ dg_status dg_cache_load(const char *path) {
                              &c.block_k, &c.group_m, &c.waves, &c.stages, &c.variant, &c.xcd_remap, &c.k_splits);
         const bool sane = n == 18 && k.M >= 0 && k.N >= 0 && k.K >= 0 && k.batch >= 0 && dtype_ok(k.in) &&
                           dtype_ok(k.out) && c.block_m > 0 && c.block_n > 0 && c.block_k > 0 && c.group_m > 0 &&
-                          c.k_splits >= 0;
+                          (c.k_splits >= 0 || c.k_splits == DG_STREAM_K);
         if (!sane) {
             ++bad;
             continue;
@@ -1084,6 +1164,15 @@ dg_status autotune_impl(const Problem &p, hipStream_t stream, int repeats, dg_co
         cands.push_back(c);
         if (c.variant != DG_VARIANT_MFMA || ws_bytes <= 0) continue;
         const int64_t tiles = ((p.M + c.block_m - 1) / c.block_m) * ((p.N + c.block_n - 1) / c.block_n) * p.batch;
+        if (tiles > cus && tiles % cus != 0) {
+            // a partial last round: stream-K shares it out
+            dg_config x = c;
+            x.k_splits = DG_STREAM_K;
+            const KernelEntry *e = find_kernel(x, p);
+            const WsLayout L = sk_layout(p.M, p.N, p.batch, x);
+            SkPlan plan;
+            if (e && e->stream_k && L.total <= ws_bytes && sk_plan(tiles, p.K, x, plan)) cands.push_back(x);
+        }
         if (tiles >= cus) continue;
         for (int sk : kSplits) {
             dg_config x = c;

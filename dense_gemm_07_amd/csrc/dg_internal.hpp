@@ -36,7 +36,7 @@ struct GemmArgs {
     int32_t splits;         // K ranges per tile, >= 1; > 1 only for the MFMA kernels
     int32_t k_chunk;        // K elements per range (a multiple of block_k when splits > 1)
     int64_t bsa, bsb, bsc;  // batch strides of A, B, C
-    float *ws;              // split-K partial tiles (fp32)
+    float *ws;              // split-K partial tiles (fp32); stream-K flags and partials
     // fused epilogue: C = act(alpha * acc + beta * R + bias)
     int32_t epi;            // 0: C = acc (the other fields are unused); 1: the general form
     int32_t act;            // dg_activation
@@ -48,6 +48,13 @@ struct GemmArgs {
     const void *bias;       // NULL: no bias
     int64_t sbias, bsbias;
     int32_t bias_per_row;   // 0: bias[j], one per column; 1: bias[i], one per row
+    // stream-K (EM_STREAMK kernels)
+    int32_t sk_groups;      // > 0: stream-K over this many workgroups (ranks); 0: one workgroup per work item
+    int32_t sk_tiles;       // tiles whose K steps are shared out; the rest are whole-tile work
+    int32_t sk_iters;       // K steps per tile, ceil(K / block_k)
+    int32_t sk_base;        // S / sk_groups, S = sk_tiles * sk_iters < 2^31
+    int32_t sk_extra;       // S % sk_groups: ranks below it take one step more
+    uint32_t sk_epoch;      // this launch's flag value (never 0)
 };
 
 // How an operand tile is fetched from global memory. The operand is viewed
@@ -73,6 +80,7 @@ struct KernelEntry {
     int32_t load_b;     // LoadMode for B (-1: any)
     LaunchFn launch;
     const char *name;
+    bool stream_k;      // also compiled as a stream-K kernel (k_splits = DG_STREAM_K)
 };
 
 // Registration hooks, one per kernel translation unit.
@@ -155,8 +163,13 @@ __host__ __device__ inline WorkItem work_item(int wg, const GemmArgs &g) {
     return w;
 }
 
+// Bytes of the stream-K flags at the start of the workspace (one 8-byte flag
+// per rank, padded to 256 bytes); the partial tiles follow.
+__host__ __device__ inline int64_t sk_flag_bytes(int groups) { return ((int64_t)groups * 8 + 255) / 256 * 256; }
+
 // Workgroups of one launch.
 inline unsigned launch_groups(const GemmArgs &g) {
+    if (g.sk_groups > 0) return (unsigned)g.sk_groups;
     return (unsigned)g.grid_m * (unsigned)g.grid_n * (unsigned)g.splits * (unsigned)g.batch;
 }
 

@@ -257,25 +257,6 @@ __device__ __forceinline__ u32x4 pack8(const uint16_t (&v)[8]) {
     return r;
 }
 
-__device__ __forceinline__ uint32_t dword_of(const u32x4 &v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// 8x8 transpose of 16-bit elements: in[j] holds row j (8 elements), out[i]
-// holds column i. v_perm_b32 selectors pick the low (even column) or high
-// (odd column) halves of two input dwords.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t d[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            d[p] = __builtin_amdgcn_perm(dword_of(in[2 * p + 1], i >> 1), dword_of(in[2 * p], i >> 1), sel);
-        out[i] = u32x4{d[0], d[1], d[2], d[3]};
-    }
-}
-
 // 16 bytes from an address that is only element (2-byte) aligned. gfx950
 // serves unaligned global vector loads; the compiler emits one
 // global_load_dwordx4 for this.
@@ -303,54 +284,31 @@ __device__ __forceinline__ u32x4 drop_elems(u32x4 v, int sh) {
 // k >= K) become +0 and are never read.
 //  LD_KU: k stride 1. Whole 8-element chunks are one 16-byte load at any
 //         element alignment; a chunk cut by K is loaded element by element.
-//  LD_RU: row stride 1. 8x8 blocks: eight 16-byte loads along the rows, then
-//         an in-register transpose; a block cut by the row count is loaded
-//         element by element.
 //  LD_GN: anything else, element loads through both strides.
 template <int ROWS, int BK, int LDK, int T, int MODE>
 struct TileLoader {
-    static_assert(MODE == LD_KU || MODE == LD_RU || MODE == LD_GN, "register-staged load modes");
+    // Row-contiguous unaligned operands (LD_RU) take the staged kernel at
+    // every tile size.
+    static_assert(MODE == LD_KU || MODE == LD_GN, "register-staged load modes");
     static constexpr int KCH = BK / 8;                   // 8-element k-chunks per row
-    static constexpr int NCH = ROWS * KCH;               // chunks per tile (KU, GN)
+    static constexpr int NCH = ROWS * KCH;               // chunks per tile
     static constexpr int PER = (NCH + T - 1) / T;
-    static constexpr int NBL = (ROWS / 8) * KCH;         // 8x8 blocks per tile (RU)
-    static constexpr int PERB = (NBL + T - 1) / T;
-    static constexpr int NREG = MODE == LD_RU ? PERB * 8 : PER;
 
-    u32x4 reg[NREG];
+    u32x4 reg[PER];
     bool okc[PER];         // LD_KU: chunk c is inside the operand (else LDS gets zeros)
     const uint16_t *base;  // element (row0, k = 0) of the operand
     int64_t srow, sk;      // element strides along rows and along k
     int rows_valid;        // rows of the tile inside the operand
     int K;
 
-    // INSIDE_K: the caller knows k0 + BK <= K and, for LD_RU, that every row
-    // of the tile is inside the operand. Then the loads have no branch: a
-    // branch around a load (the element loads at the edges) makes the
+    // INSIDE_K: the caller knows k0 + BK <= K. Then the loads have no branch:
+    // a branch around a load (the element loads at the edges) makes the
     // compiler wait for the load where the two paths join, i.e. at once.
     // LD_KU chunks are one 16-byte load each from a row clamped into the
     // operand; the row mask is applied when the chunk is written to LDS
-    // (store). LD_RU blocks past the tile's block count repeat the last
-    // block's loads (store skips them).
+    // (store).
     template <bool INSIDE_K = false>
     __device__ __forceinline__ void load(int tid, int k0) {
-        if constexpr (MODE == LD_RU && INSIDE_K) {
-#pragma unroll
-            for (int b = 0; b < PERB; ++b) {
-                const int q = b * T + tid;
-                const int qc = (NBL % T == 0) ? q : (q < NBL ? q : NBL - 1);
-                const int kb = qc % KCH, r0 = (qc / KCH) * 8;
-                u32x4 raw[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    raw[j] = load16_unaligned(base + (int64_t)(k0 + kb * 8 + j) * sk + r0);
-                u32x4 t[8];
-                transpose8x8(raw, t);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) reg[b * 8 + i] = t[i];
-            }
-            return;
-        }
         if constexpr (MODE == LD_KU && INSIDE_K) {
 #pragma unroll
             for (int c = 0; c < PER; ++c) {
@@ -366,90 +324,45 @@ struct TileLoader {
 #pragma unroll
             for (int c = 0; c < PER; ++c) okc[c] = true;
         }
-        if constexpr (MODE == LD_RU) {
 #pragma unroll
-            for (int b = 0; b < PERB; ++b) {
-                const int q = b * T + tid;
-                u32x4 raw[8];
-                const int kb = q % KCH, rb = q / KCH;
-                const int r0 = rb * 8;
-                const bool qok = (NBL % T == 0) || q < NBL;
+        for (int c = 0; c < PER; ++c) {
+            const int q = c * T + tid;
+            const int r = q / KCH, kc = q % KCH;
+            const int k = k0 + kc * 8;
+            const bool ok = ((NCH % T == 0) || q < NCH) && r < rows_valid;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (MODE == LD_KU) {
+                const uint16_t *p = base + (int64_t)r * srow + k;
+                if (ok && k + 8 <= K) {
+                    v = load16_unaligned(p);
+                } else if (ok && k < K) {
+                    uint16_t e8[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int k = k0 + kb * 8 + j;
-                    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                    if (qok && k < K) {
-                        const uint16_t *p = base + (int64_t)k * sk + r0;
-                        if (r0 + 8 <= rows_valid) {
-                            v = load16_unaligned(p);
-                        } else if (r0 < rows_valid) {
-                            uint16_t e8[8];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) e8[e] = (r0 + e < rows_valid) ? p[e] : (uint16_t)0;
-                            v = pack8(e8);
-                        }
-                    }
-                    raw[j] = v;
+                    for (int e = 0; e < 8; ++e) e8[e] = (k + e < K) ? p[e] : (uint16_t)0;
+                    v = pack8(e8);
                 }
-                u32x4 t[8];
-                transpose8x8(raw, t);
+            } else {  // LD_GN
+                if (ok) {
+                    const uint16_t *p = base + (int64_t)r * srow;
+                    uint16_t e8[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) reg[b * 8 + i] = t[i];
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < PER; ++c) {
-                const int q = c * T + tid;
-                const int r = q / KCH, kc = q % KCH;
-                const int k = k0 + kc * 8;
-                const bool ok = ((NCH % T == 0) || q < NCH) && r < rows_valid;
-                u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                if (MODE == LD_KU) {
-                    const uint16_t *p = base + (int64_t)r * srow + k;
-                    if (ok && k + 8 <= K) {
-                        v = load16_unaligned(p);
-                    } else if (ok && k < K) {
-                        uint16_t e8[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) e8[e] = (k + e < K) ? p[e] : (uint16_t)0;
-                        v = pack8(e8);
-                    }
-                } else {  // LD_GN
-                    if (ok) {
-                        const uint16_t *p = base + (int64_t)r * srow;
-                        uint16_t e8[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) e8[e] = (k + e < K) ? p[(int64_t)(k + e) * sk] : (uint16_t)0;
-                        v = pack8(e8);
-                    }
+                    for (int e = 0; e < 8; ++e) e8[e] = (k + e < K) ? p[(int64_t)(k + e) * sk] : (uint16_t)0;
+                    v = pack8(e8);
                 }
-                reg[c] = v;
             }
+            reg[c] = v;
         }
     }
 
     __device__ __forceinline__ void store(int tid, uint16_t *lds) const {
-        if constexpr (MODE == LD_RU) {
 #pragma unroll
-            for (int b = 0; b < PERB; ++b) {
-                const int q = b * T + tid;
-                if ((NBL % T == 0) || q < NBL) {
-                    const int kb = q % KCH, rb = q / KCH;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        *reinterpret_cast<u32x4 *>(lds + (rb * 8 + i) * LDK + kb * 8) = reg[b * 8 + i];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < PER; ++c) {
-                const int q = c * T + tid;
-                if ((NCH % T == 0) || q < NCH) {
-                    const int r = q / KCH, kc = q % KCH;
-                    u32x4 v = reg[c];
-                    if constexpr (MODE == LD_KU) v = okc[c] ? v : u32x4{0u, 0u, 0u, 0u};
-                    *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = v;
-                }
+        for (int c = 0; c < PER; ++c) {
+            const int q = c * T + tid;
+            if ((NCH % T == 0) || q < NCH) {
+                const int r = q / KCH, kc = q % KCH;
+                u32x4 v = reg[c];
+                if constexpr (MODE == LD_KU) v = okc[c] ? v : u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = v;
             }
         }
     }
@@ -893,7 +806,7 @@ __device__ __forceinline__ void split_store(const GemmArgs &g, const WorkItem &w
 // arguments: the fused epilogue's registers and code would otherwise change
 // how the compiler schedules the K loop of the plain kernel (measured: 9%
 // slower at 4096^3).
-enum EpiMode : int { EM_STORE = 0, EM_FUSED = 1, EM_SPLIT = 2 };
+enum EpiMode : int { EM_STORE = 0, EM_FUSED = 1, EM_SPLIT = 2, EM_STREAMK = 3 };
 
 // Plain stores straight from the accumulator registers.
 template <int BM, int BN, int WM, int WN, int FM, int FN>
@@ -927,22 +840,206 @@ __device__ __forceinline__ void finish_tile(const GemmArgs &g, const WorkItem &w
     else write_plain<BM, BN, WM, WN, FM, FN>(g, w, acc, m0, n0);
 }
 
-// WM x WN waves, each owning a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.
-template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int EM>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
+// Buffer resources (raw, 32-bit data format) for the buffer load and store
+// builtins.
+constexpr int kOobOffset = (int)0x80000000;  // buffer offset >= num_records: loads zero
+constexpr int kNumRecords = 0x7fffffff;
+constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data format
+
+// s_waitcnt vmcnt(0) (expcnt/lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---- stream-K ------------------------------------------------------------------
+// A persistent grid of G workgroups (at most one per CU, so all are resident
+// at once) shares out the tiles' K steps evenly instead of whole tiles, so a
+// tile count just past a multiple of G does not cost a whole extra round of
+// tiles (the wave quantisation that shapes needing their own configs run
+// into, "Triton：04 Matmul、Autotune 与 PyTorch 集成"). Rank r of G:
+//  1. computes whole tiles sk_tiles + r, sk_tiles + r + G, ... (all K);
+//  2. takes its share of the S = sk_tiles * sk_iters K steps of the first
+//     sk_tiles tiles, numbered tile-major: ranks below S % G take S / G + 1
+//     consecutive steps, the others S / G (S < 2^31, checked on the host).
+//     The host shares the partial last round together with one whole round
+//     (so every rank takes one to two tiles' steps and a tile has at most
+//     three pieces), and launches at most two ranks per tile when there are
+//     fewer tiles than CUs. The range is split at
+//     tile boundaries into pieces. A piece that starts inside its tile
+//     (only a rank's first piece can) stores its fp32 partial tile in slot r
+//     and then raises flag r. A piece that starts at the tile's first K step
+//     belongs to the tile's owner: it adds the partials of the ranks that
+//     cover the rest of the tile, in rank order (= K order, so the result
+//     does not depend on timing), and runs the epilogue.
+// An owner waits only on higher ranks' first pieces, which wait on nothing,
+// so the grid cannot deadlock while all its workgroups are resident; the wait
+// is still bounded (a partial that never arrives leaves NaN in the tile).
+// Partials and flags cross XCDs: they are written and read with agent-scope
+// atomic accesses, which bypass the non-coherent caches line by line, and
+// the flag is stored only after the partial's stores have completed. This
+// avoids the release/acquire fences, which write back or invalidate a
+// whole L2.
+//
+// Workspace: G 8-byte flags (padded to 256 bytes), then G partial tiles in
+// split_store's layout. A flag holds the launch's epoch in its low word and
+// the epoch's complement in its high word, so flags left by earlier launches
+// (or other data) never read as raised.
+constexpr int kSkSpinLimit = 1 << 20;
+constexpr int kSc1 = 16;  // buffer cache-policy operand: the sc1 (agent-scope coherent) bit
+
+// Bit casts through a by-value scalar: applied directly to a vector element
+// (acc[i][j][r], d[c]), __builtin_bit_cast reads element 0 whatever the index
+// (seen with this compiler), so elements always pass through these.
+__device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bits_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// (product, tile) of stream-K tile number t: products outermost, the
+// group-major order within a product.
+__device__ __forceinline__ WorkItem sk_tile(int t, const GemmArgs &g) {
+    const int tiles = g.grid_m * g.grid_n;
+    WorkItem w;
+    w.prod = t / tiles;
+    w.split = 0;
+    group_major(t - w.prod * tiles, g.grid_m, g.grid_n, g.group_m, w.pm, w.pn);
+    w.slot = w.prod * tiles + w.pm * g.grid_n + w.pn;
+    return w;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int FM, int FN, int CAP, typename Body>
+__device__ __forceinline__ void stream_k(const GemmArgs &g, float *st, Body &body) {
+    constexpr int T = WM * WN * 64;
+    constexpr int V = FM * FN * 4;  // float4s per thread in a partial
+    const int G = gridDim.x;
+    const int r = (g.xcd_remap && g.num_xcd > 1) ? xcd_rank(blockIdx.x, G, g.num_xcd) : (int)blockIdx.x;
+    const int total = g.grid_m * g.grid_n * g.batch;
+    const int I = g.sk_iters;
+    uint64_t *flags = reinterpret_cast<uint64_t *>(g.ws);
+    float *parts = reinterpret_cast<float *>(reinterpret_cast<char *>(g.ws) + sk_flag_bytes(G));
+    const uint64_t mark = ((uint64_t)(~g.sk_epoch) << 32) | g.sk_epoch;
+    // One call site for the tile body: whole tiles first, then the pieces.
+    const int base = g.sk_base, extra = g.sk_extra;  // S / G, S % G
+    auto share_begin = [&](int q) { return q * base + min(q, extra); };
+    int it = share_begin(r);
+    const int it1 = share_begin(r + 1);
+    int next_whole = g.sk_tiles + r;
+    for (bool first = true;; first = false) {
+        int t, kb, ke;
+        bool whole;
+        if (next_whole < total) {
+            t = next_whole;
+            kb = 0;
+            ke = I;
+            whole = true;
+            next_whole += G;
+        } else if (it < it1) {
+            t = it / I;
+            kb = it - t * I;            // first K step of the piece
+            ke = min(I, it1 - t * I);   // one past its last
+            whole = false;
+            it = t * I + ke;
+        } else {
+            break;
+        }
+        if (!first) __syncthreads();  // the previous tile is done with the LDS
+        const WorkItem w = sk_tile(t, g);
+        f32x16 acc[FM][FN];
+        body(w, kb * BK, min(g.K, ke * BK) - kb * BK, acc);
+        // Partials move as 16-byte buffer accesses with the agent-scope
+        // coherence bit (sc1): float4 v of thread t at byte (v * T + t) * 16 of
+        // the rank's slot, the register offset fixed and the slice offset a
+        // scalar, so no per-access address registers.
+        const int voff = threadIdx.x * 16;
+        if (kb > 0) {
+            const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+                parts + (int64_t)r * (V * T * 4), 0, V * T * 16, kRsrcWord3);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        u32x4 d;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) d[c] = f32_bits(acc[i][j][4 * q + c]);
+                        __builtin_amdgcn_raw_buffer_store_b128(d, mine, voff, ((i * FN + j) * 4 + q) * T * 16,
+                                                               kSc1);
+                    }
+            wait_vmcnt0();  // this thread's stores have completed
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_store(flags + r, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            continue;
+        }
+        if (!whole) {
+            const int tile_end = (t + 1) * I;
+            for (int q = r + 1; q < G; ++q) {
+                const int q0 = share_begin(q);
+                if (q0 >= tile_end) break;
+                if (share_begin(q + 1) == q0) continue;  // rank q has no steps
+                // Each wave watches the flag itself (lane 0) and reads the
+                // partial after seeing it raised.
+                int spins = 0;
+                if ((threadIdx.x & 63) == 0)
+                    while (__hip_atomic_load(flags + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != mark &&
+                           ++spins < kSkSpinLimit)
+                        __builtin_amdgcn_s_sleep(2);
+                const bool lost = __builtin_amdgcn_readfirstlane(spins) >= kSkSpinLimit;
+                const __amdgpu_buffer_rsrc_t theirs = __builtin_amdgcn_make_buffer_rsrc(
+                    parts + (int64_t)q * (V * T * 4), 0, V * T * 16, kRsrcWord3);
+                // CH float4s requested together (the whole partial of a small
+                // tile, 16 at a time of a large one), then added.
+                constexpr int CH = V < 16 ? V : 16;
+#pragma unroll
+                for (int v0 = 0; v0 < V; v0 += CH) {
+                    u32x4 d[CH];
+#pragma unroll
+                    for (int u = 0; u < CH; ++u)
+                        d[u] = __builtin_amdgcn_raw_buffer_load_b128(theirs, voff, (v0 + u) * T * 16, kSc1);
+#pragma unroll
+                    for (int u = 0; u < CH; ++u) {
+                        const int v = v0 + u, i = v / (FN * 4), j = (v / 4) % FN, q4 = v % 4;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            acc[i][j][4 * q4 + c] =
+                                lost ? __builtin_nanf("") : acc[i][j][4 * q4 + c] + bits_f32(d[u][c]);
+                    }
+                }
+            }
+        }
+        write_tile<BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, w.pm * BM, w.pn * BN);
+    }
+}
+
+// The work of one launch: one tile (or K range) per workgroup, or stream-K.
+// body(w, k_begin, kl, acc) computes tile w over k in [k_begin, k_begin + kl).
+template <int EM, int BM, int BN, int BK, int WM, int WN, int FM, int FN, int CAP, typename Body>
+__device__ __forceinline__ void run_tiles(const GemmArgs &g, float *st, Body &&body) {
+    if constexpr (EM == EM_STREAMK) {
+        stream_k<BM, BN, BK, WM, WN, FM, FN, CAP>(g, st, body);
+    } else {
+        const WorkItem w = work_item(blockIdx.x, g);
+        const int k_begin = w.split * g.k_chunk;
+        const int kl = min(g.K - k_begin, g.k_chunk);  // this workgroup's K range
+        f32x16 acc[FM][FN];
+        body(w, k_begin, kl, acc);
+        // Epilogue: fp32 accumulators -> C's dtype, masked to C's view.
+        finish_tile<EM, BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, w.pm * BM, w.pn * BN);
+    }
+}
+
+// One output tile of the register-staged kernel: WM x WN waves, each owning
+// a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks; acc receives the tile's
+// sum over k in [k_begin, k_begin + kl). LDK is the LDS row pitch in
+// elements: +16 B breaks the bank pattern of 128 B rows.
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB>
+__device__ __forceinline__ void mfma_reg_tile(const GemmArgs &g, const WorkItem &w, int k_begin, int kl,
+                                              uint16_t (&lds)[2][(BM + BN) * (BK + 8)],
+                                              f32x16 (&acc)[BM / WM / 32][BN / WN / 32]) {
     constexpr int T = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int LDK = BK + 8;  // row pitch (elements): +16 B breaks the bank pattern of 128 B rows
+    constexpr int LDK = BK + 8;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "8-row blocks");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * LDK];
-
-    const WorkItem w = work_item(blockIdx.x, g);
     const int m0 = w.pm * BM, n0 = w.pn * BN;
-    const int k_begin = w.split * g.k_chunk;
-    const int kl = min(g.K - k_begin, g.k_chunk);  // this workgroup's K range
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -979,7 +1076,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
         lb[p].K = kl;
     }
 
-    f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -988,15 +1084,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = (kl + BK - 1) / BK;
-    // Slices [0, n_fast) take the branch-free loads: wholly inside K, and a
-    // row-contiguous operand's tile has all its rows.
-    const bool full_rows = (LA != LD_RU || la[0].rows_valid == BM) && (LB != LD_RU || lb[0].rows_valid == BN);
-    const int n_fast = full_rows ? kl / BK : 0;
+    // Slices [0, n_fast) take the branch-free loads: wholly inside K.
+    const int n_fast = kl / BK;
 
 #pragma unroll
     for (int p = 0; p + 1 < P; ++p) {
         if (!DEEP && p < nk) {
-            if (full_rows && (p + 1) * BK <= kl) {  // p < n_fast
+            if ((p + 1) * BK <= kl) {  // p < n_fast
                 la[p % NSET].template load<true>(tid, p * BK);
                 lb[p % NSET].template load<true>(tid, p * BK);
             } else {
@@ -1088,8 +1182,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
         // rest, guarded.
         int kt = 0;
         // LD_GN has no branch-free load (both operands use it or neither).
-        // At BK 32 the compiler spills this loop heavily with LD_RU, so
-        // those tiles keep the guarded loop.
         if constexpr (LA != LD_GN && BK >= 64)
         for (; kt + 2 <= n_fast; ++kt) {
             la[0].template load<true>(tid, (kt + 1) * BK);
@@ -1138,7 +1230,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
                 if (kt >= nk) break;
                 if (kt + P - 1 < nk) {
                     const int k0 = (kt + P - 1) * BK;
-                    if (full_rows && k0 + BK <= kl) {  // slice below n_fast
+                    if (k0 + BK <= kl) {  // slice below n_fast
                         la[(u + P - 1) % P].template load<true>(tid, k0);
                         lb[(u + P - 1) % P].template load<true>(tid, k0);
                     } else {
@@ -1155,10 +1247,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
             }
         }
     }
+}
 
-    // Epilogue: fp32 accumulators -> C's dtype, masked to C's view.
-    finish_tile<EM, BM, BN, WM, WN, FM, FN, (int)sizeof(lds)>(g, w, acc, reinterpret_cast<float *>(&lds[0][0]), m0,
-                                                              n0);
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int EM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma(GemmArgs g) {
+    constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * (BK + 8)];
+    run_tiles<EM, BM, BN, BK, WM, WN, FM, FN, (int)sizeof(lds)>(
+        g, reinterpret_cast<float *>(&lds[0][0]), [&](const WorkItem &w, int k_begin, int kl, f32x16(&acc)[FM][FN]) {
+            mfma_reg_tile<TI, BM, BN, BK, WM, WN, LA, LB>(g, w, k_begin, kl, lds, acc);
+        });
 }
 
 // ============================================================================
@@ -1186,12 +1284,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-constexpr int kOobOffset = (int)0x80000000;  // buffer offset >= num_records: loads zero
-constexpr int kNumRecords = 0x7fffffff;
-constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data format
-
-// s_waitcnt vmcnt(0) (expcnt/lgkmcnt left at their maxima).
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int ROWS, int BK>
 struct KTile {
@@ -1386,8 +1478,12 @@ __device__ __forceinline__ void interleave_mfma() {
 // kt-1 used, then multiplies slice kt. Slices past K are queued as
 // out-of-range loads (zeros into a free buffer) so that every step issues the
 // same number of loads and the wait count stays a constant.
-template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S, int EM>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
+// One output tile of the direct kernel; acc receives the tile's sum over k in
+// [k_begin, k_begin + kl). `lds` holds S stages of A_BYTES + B_BYTES.
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
+__device__ __forceinline__ void mfma_lds_tile(const GemmArgs &g, const WorkItem &w, int k_begin, int kl,
+                                              char (&lds)[S * (BM + BN) * BK * 2],
+                                              f32x16 (&acc)[BM / WM / 32][BN / WN / 32]) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -1396,16 +1492,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
     static_assert(S >= 2, "at least two stages");
 
-    // One LDS object only: the compiler proves the fragment reads independent
-    // of the in-flight LDS loads per object, and a second __shared__ variable
-    // makes it wait for every load before each read. The epilogue reuses this
-    // LDS once the K loop is done.
-    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
-
-    const WorkItem w = work_item(blockIdx.x, g);
     const int m0 = w.pm * BM, n0 = w.pn * BN;
-    const int k_begin = w.split * g.k_chunk;
-    const int kl = min(g.K - k_begin, g.k_chunk);  // this workgroup's K range
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1433,7 +1520,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
                 (int64_t)k_begin * g.sbk,
             g.sbn, g.sbk, min(BN, g.N - n0), loader ? wave : 0, lane);
 
-    f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1534,8 +1620,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
         step(std::true_type{}, lds + fill * STAGE, lds + cur * STAGE, lds + next * STAGE, kt);
     }
     wait_vmcnt<0>();  // the out-of-range tail loads must land before the workgroup can exit
+}
 
-    finish_tile<EM, BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
+template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S, int EM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_lds(GemmArgs g) {
+    constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+    // One LDS object only: the compiler proves the fragment reads independent
+    // of the in-flight LDS loads per object, and a second __shared__ variable
+    // makes it wait for every load before each read. The epilogue reuses this
+    // LDS once the K loop is done.
+    __shared__ __attribute__((aligned(1024))) char lds[S * (BM + BN) * BK * 2];
+    run_tiles<EM, BM, BN, BK, WM, WN, FM, FN, (int)sizeof(lds)>(
+        g, reinterpret_cast<float *>(lds), [&](const WorkItem &w, int k_begin, int kl, f32x16(&acc)[FM][FN]) {
+            mfma_lds_tile<TI, BM, BN, BK, WM, WN, LA, LB, S>(g, w, k_begin, kl, lds, acc);
+        });
 }
 
 // ============================================================================
@@ -1647,7 +1745,10 @@ constexpr int staged_sets() {
     return (BM * BN >= 256 * 256 && BK >= 64) ? 1 : (BM * BN >= 128 * 128 ? 2 : 3);
 }
 
-// WM x WN waves (every wave loads).
+// WM x WN waves (every wave loads). One tile per workgroup only (no
+// stream-K instantiation): written as a tile function called from the
+// launch loop, the 256x256 tile's registers overflowed (the compiler spilled
+// 4-31 registers, some inside the K loop), where this form spills none.
 template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int EM>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_rs(GemmArgs g) {
     constexpr int NW = WM * WN;

@@ -12,15 +12,20 @@ constexpr bool direct_to_lds() {
     return (LA == LD_KC || LA == LD_RC) && (LB == LD_KC || LB == LD_RC);
 }
 
-// Large tiles with contiguous (but not 16-byte aligned) operands stage them
-// through registers into the direct kernel's LDS formats; small tiles and
-// element-wise (LD_GN) operands keep the padded-row register kernel (for the
-// 64x64 tiles of a 1000x1500x777 product the staged format measured 10 %
-// slower: their short steps are bound by per-step costs, not by the LDS
-// format).
+// Contiguous (but not 16-byte aligned) operands are staged through registers
+// into the direct kernel's LDS formats on large tiles, and on small tiles
+// when one operand is row-contiguous; small tiles with both operands
+// k-contiguous, and element-wise (LD_GN) operands, keep the padded-row
+// register kernel. Measured on MI355X: for the 64x64 tiles of a
+// 1000x1500x777 product with k-contiguous operands the staged format is 10 %
+// slower (short steps bound by per-step costs); with a row-contiguous B
+// (1000x1500x2048, B row-major) the padded-row kernel's 8x8 register
+// transposes, done by every thread of a 256-thread tile for 64 blocks, made
+// it 5x slower than the staged format.
 template <int BM, int BN, int LA, int LB>
 constexpr bool staged_direct_format() {
-    return BM * BN >= 128 * 128 && (LA == LD_KU || LA == LD_RU) && (LB == LD_KU || LB == LD_RU);
+    return (BM * BN >= 128 * 128 || LA == LD_RU || LB == LD_RU) && (LA == LD_KU || LA == LD_RU) &&
+           (LB == LD_KU || LB == LD_RU);
 }
 
 template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S, int EM>
@@ -36,10 +41,30 @@ void launch_mode(const GemmArgs &g, hipStream_t s) {
         hipLaunchKernelGGL((gemm_mfma<TI, BM, BN, BK, WM, WN, LA, LB, EM>), dim3(groups), dim3(WM * WN * 64), 0, s, g);
 }
 
-// The instantiation for the arguments: split-K partials, fused epilogue, or
-// plain stores.
+// Tile shapes that are also compiled as stream-K kernels: the 64x64 tile the
+// heuristic takes for small problems and the 128x128 tile, at BK 64 (for the
+// register-staged kernel, whose pipeline depth is fixed, the two-stage entry;
+// for the direct kernel, the 64x64 tile's four stages), on the direct and the
+// padded-row register kernels. Not the 256x256 tile (with the piece loop
+// around it, its eight waves' registers overflow: the compiler spilled inside
+// the K loop), nor the staged kernel (the same, at 256x256).
+template <int BM, int BN, int BK, int S, int LA, int LB>
+constexpr bool has_stream_k() {
+    if (BK != 64 || staged_direct_format<BM, BN, LA, LB>()) return false;
+    if (BM == 64 && BN == 64) return direct_to_lds<LA, LB>() ? S == 4 : S == 2;
+    return BM == 128 && BN == 128 && S == 2;
+}
+
+// The instantiation for the arguments: stream-K, split-K partials, fused
+// epilogue, or plain stores.
 template <typename TI, int BM, int BN, int BK, int WM, int WN, int LA, int LB, int S>
 hipError_t launch_mfma(const GemmArgs &g, hipStream_t s) {
+    if constexpr (has_stream_k<BM, BN, BK, S, LA, LB>())
+        if (g.sk_groups > 0) {
+            launch_mode<TI, BM, BN, BK, WM, WN, LA, LB, S, EM_STREAMK>(g, s);
+            return hipGetLastError();
+        }
+    if (g.sk_groups > 0) return hipErrorInvalidValue;  // the host checks KernelEntry::stream_k first
     if (g.splits > 1) launch_mode<TI, BM, BN, BK, WM, WN, LA, LB, S, EM_SPLIT>(g, s);
     else if (g.epi) launch_mode<TI, BM, BN, BK, WM, WN, LA, LB, S, EM_FUSED>(g, s);
     else launch_mode<TI, BM, BN, BK, WM, WN, LA, LB, S, EM_STORE>(g, s);
@@ -52,7 +77,8 @@ void add_mfma(std::vector<KernelEntry> &out) {
                               &launch_mfma<TI, BM, BN, BK, WM, WN, LA, LB, S>,
                               direct_to_lds<LA, LB>()                   ? "gemm_mfma_lds"
                               : staged_direct_format<BM, BN, LA, LB>() ? "gemm_mfma_rs"
-                                                                         : "gemm_mfma"});
+                                                                         : "gemm_mfma",
+                              has_stream_k<BM, BN, BK, S, LA, LB>()});
 }
 
 // Every tile shape has a two-stage kernel for every load-mode pair (the

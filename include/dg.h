@@ -93,7 +93,24 @@ enum {
  *             second kernel sums the partials in range order (deterministic)
  *             and runs the epilogue. Needs a workspace (dg_gemm_ex); MFMA
  *             kernels only.
+ *             DG_STREAM_K = stream-K: one workgroup per CU (at most two
+ *             per tile). Each computes whole tiles while more than one
+ *             whole round of one tile per CU remains; the K steps of the
+ *             rest (the last, partial round and one whole round before it,
+ *             or every tile when there are fewer tiles than CUs) are shared
+ *             out evenly over the workgroups, so a tile is cut into at most
+ *             three pieces; a tile's owner adds the other workgroups' fp32
+ *             partials in K order (deterministic) and runs the epilogue.
+ *             One kernel; needs a workspace (dg_gemm_ex). MFMA kernels with
+ *             block_k 64 and block 64x64 (4 stages for the direct-to-LDS
+ *             kernel, 2 otherwise) or 128x128 (2 stages).
+ *             Splitting K follows from a tile being the sum of its K-slice
+ *             partials ("用 Triton 写 GPU Kernel：从 Vector Add、Softmax 到
+ *             MatMul" §3.3); sharing out the partial last round answers the
+ *             shape-dependence of the best config ("Triton：04 Matmul、
+ *             Autotune 与 PyTorch 集成").
  */
+#define DG_STREAM_K (-1)
 typedef struct dg_config {
     int32_t block_m, block_n, block_k;
     int32_t group_m;
@@ -230,17 +247,23 @@ typedef struct dg_batch {
  * the library's choice, as dg_gemm) and an optional workspace.
  *
  * workspace / workspace_bytes: DEVICE memory, 256-byte aligned, for split-K
- * (config k_splits > 1; size from dg_workspace_size). NULL / 0 if none.
+ * (config k_splits > 1) and stream-K (k_splits = DG_STREAM_K); size from
+ * dg_workspace_size. NULL / 0 if none.
  * With cfg == NULL and a workspace, the library may choose split-K for
  * problems whose output tiles leave most of the GPU idle and whose K is long,
- * when the workspace is large enough; without one it never splits. Split-K
- * runs as two kernels on `stream`: the K ranges store fp32 partial tiles in
- * the workspace, then a reduction kernel adds each tile's partials in range
- * order (deterministic) and applies the epilogue. The workspace needs no
+ * when the workspace is large enough; without one it never splits. It never
+ * chooses stream-K by itself (measured slower than the unsplit kernels on
+ * MI355X); dg_autotune_ex times it. Split-K runs as two kernels on
+ * `stream`: the K ranges store fp32 partial tiles in the workspace, then a
+ * reduction kernel adds each tile's partials in range order (deterministic)
+ * and applies the epilogue. Stream-K is one kernel; it keeps its partial
+ * tiles and per-workgroup flags in the workspace (each launch writes its own
+ * flag values, so nothing needs resetting). The workspace needs no
  * initialisation. Calls that share a workspace must not run concurrently
  * (issue them on one stream, or synchronise). The library never allocates.
- * An explicit config with k_splits > 1 and no (or too small a) workspace is
- * DG_ERR_INVALID_VALUE; with a SIMT config it is DG_ERR_NO_CONFIG.
+ * An explicit config with k_splits > 1 or DG_STREAM_K and no (or too small a)
+ * workspace is DG_ERR_INVALID_VALUE; with a SIMT config, or DG_STREAM_K on a
+ * tile shape compiled without it, it is DG_ERR_NO_CONFIG.
  */
 dg_status dg_gemm_ex(int64_t M, int64_t N, int64_t K,
                      const void *A, int64_t stride_am, int64_t stride_ak,
@@ -281,7 +304,8 @@ dg_status dg_gemm_ex_noalloc(int64_t M, int64_t N, int64_t K,
 /*
  * dg_autotune for a dg_gemm_ex problem (epilogue and batch included in every
  * timed launch). With a workspace, the candidates also include split-K
- * counts (2, 4, 8, 16) for tile shapes that do not fill the GPU. The winner
+ * counts (2, 4, 8, 16) for tile shapes that do not fill the GPU, and
+ * stream-K for tile shapes whose last round of tiles is partial. The winner
  * is cached under (M, N, K, batch count, dtypes, layouts); a later dg_gemm_ex
  * with cfg == NULL uses it (unsplit if that call's workspace is too small).
  * An epilogue that reads C (beta != 0 and no separate residual) is
@@ -307,6 +331,9 @@ dg_status dg_autotune_ex(int64_t M, int64_t N, int64_t K,
  * block_m * block_n * 4. K is cut into ranges of k_chunk = block_k *
  * ceil(ceil(K / k_splits) / block_k) elements; the ranges actually used
  * number ceil(K / k_chunk) (at most k_splits; 1 when K <= block_k).
+ * Stream-K (k_splits = DG_STREAM_K): with G = the current device's CU count,
+ * 8 * G bytes of flags rounded up to 256, then G partial tiles of
+ * block_m * block_n * 4 bytes (0 for an empty problem).
  */
 dg_status dg_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch_count, const dg_config *cfg,
                             int64_t *bytes);

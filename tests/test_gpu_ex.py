@@ -215,11 +215,12 @@ def _offset_view(t, colmajor, pad):
 @pytest.mark.parametrize("shape", [(257, 263, 777), (300, 9, 520), (9, 300, 100), (515, 130, 1000)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_staged_large_tiles_bit_exact(shape):
-    """Large tiles with contiguous operands off 16-byte alignment: registers
-    stage them into the direct kernel's LDS formats. Each operand k-contiguous
-    or row-contiguous; edge tiles with fewer than 8 valid rows, K tails that
-    are not multiples of 8, products of less than one tile. Integers,
-    bit-exact."""
+    """Contiguous operands off 16-byte alignment staged through registers into
+    the direct kernel's LDS formats: large tiles, and 64x64 tiles when an
+    operand is row-contiguous (the 64x64 configs run the padded-row register
+    kernel when both are k-contiguous). Each operand k-contiguous or
+    row-contiguous; edge tiles with fewer than 8 valid rows, K tails that are
+    not multiples of 8, products of less than one tile. Integers, bit-exact."""
     M, N, K = shape
     a, b = inputs.integer_operands(M, N, K, "bf16", seed=M + 3 * N + 7 * K)
     want32 = ref_product(a, b, "bf16")
@@ -228,7 +229,7 @@ def test_staged_large_tiles_bit_exact(shape):
             ad = _offset_view(a, a_col, 3)
             bd = _offset_view(b, b_col, 5)
             for cfg_shape in [(256, 256, 64, 2), (256, 256, 32, 2), (128, 128, 64, 2), (256, 128, 64, 2),
-                              (128, 256, 64, 2)]:
+                              (128, 256, 64, 2), (64, 64, 64, 2), (64, 64, 32, 2)]:
                 cfg = config("bf16", *cfg_shape)
                 for out_dtype in ("f32", "bf16"):
                     what = f"{shape} A {'col' if a_col else 'row'} B {'col' if b_col else 'row'} {cfg_shape} -> {out_dtype}"

@@ -179,9 +179,10 @@ def test_cache_load_select_save_roundtrip(tmp_path):
     f.write_text("dg-config-cache 2\n"
                  "4096 4096 4096 1 2 2 0 1 0  128 128 64 4 4 2 1 0 1\n"
                  "1024 1024 1024 1 2 2 0 1 0  128 128 64 8 4 2 1 1 4\n"
+                 "1000 1500 777 1 2 2 3 3 0  64 64 64 8 4 4 1 1 -1\n"
                  "this line is garbage\n")
     dg.cache_load(str(f))
-    assert dg.cache_size() == 2
+    assert dg.cache_size() == 3
     assert b"malformed" in dg.library().dg_last_error()
     c, hit = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (4096, 1), (4096, 1), BF16, BF16)
     assert hit and (c.block_m, c.block_n, c.group_m, c.xcd_remap) == (128, 128, 4, 0)
@@ -191,15 +192,23 @@ def test_cache_load_select_save_roundtrip(tmp_path):
     # a cached split-K config runs unsplit where the call has no workspace
     c3, hit3 = dg.select_config_raw(1024, 1024, 1024, (1024, 1), (1024, 1), (1024, 1), BF16, BF16)
     assert hit3 and (c3.block_m, c3.k_splits) == (128, 1)
+    # a cached stream-K config (k-contiguous unaligned operands, layout modes 3/3)
+    ws = dict(batch=1, workspace_bytes=1 << 30)
+    c4, hit4 = dg.select_config_ex(1000, 1500, 777, (777, 1), (1, 777), (1500, 1), BF16, BF16, **ws)
+    assert hit4 and c4.k_splits == dg.STREAM_K, c4
+    c5, _ = dg.select_config_ex(1000, 1500, 777, (777, 1), (1, 777), (1500, 1), BF16, BF16, batch=1,
+                                workspace_bytes=1024)
+    assert c5.k_splits == 1  # no room for its workspace: unsplit
     out = tmp_path / "saved.txt"
     dg.cache_save(str(out))
     lines = out.read_text().splitlines()
-    assert lines[0] == "dg-config-cache 2" and len(lines) == 3
+    assert lines[0] == "dg-config-cache 2" and len(lines) == 4
     assert any(ln.split()[-1] == "4" for ln in lines[1:])  # k_splits survives the round trip
+    assert any(ln.split()[-1] == "-1" for ln in lines[1:])
     dg.cache_clear()
     assert dg.cache_size() == 0
     dg.cache_load(str(out))
-    assert dg.cache_size() == 2
+    assert dg.cache_size() == 3
     dg.cache_clear()
 
 
@@ -308,6 +317,34 @@ def test_workspace_size_arithmetic():
     assert dg.workspace_size(1024, 1024, 64, 1, cfg) == 0
     assert dg.workspace_size(1024, 1024, 4096, 1, mfma_cfg(splits=1)) == 0
     assert dg.workspace_size(0, 1024, 4096, 1, cfg) == 0
+
+
+def test_stream_k_argument_errors_and_workspace_size():
+    """Stream-K (k_splits = DG_STREAM_K): a workspace of 8 bytes of flag per
+    CU rounded up to 256, then one partial tile per CU (256 CUs on MI355X, and
+    the library's assumption without a device); checked before any launch."""
+    sk = mfma_cfg(128, 128, 64, splits=dg.STREAM_K)
+    need = dg.workspace_size(1024, 1024, 1024, 1, sk)
+    assert need == 256 * 8 + 256 * 128 * 128 * 4
+    assert dg.workspace_size(0, 1024, 1024, 1, sk) == 0
+    assert gemm_ex_status(K=4096, cfg=sk) == INVALID  # no workspace
+    assert b"stream-K" in dg.library().dg_last_error()
+    assert gemm_ex_status(K=4096, cfg=sk, ws=FAKE, ws_bytes=need - 1) == INVALID
+    assert gemm_ex_status(K=4096, cfg=sk, ws=FAKE + 16, ws_bytes=need) == INVALID  # misaligned
+    # tile shapes compiled without a stream-K kernel
+    for bm, bk, stages in [(256, 64, 2), (128, 64, 3)]:
+        c = next(x for x in dg.candidates(BF16, BF16) if (x.block_m, x.block_n, x.block_k, x.stages) == (bm, bm, bk, stages))
+        c.k_splits = dg.STREAM_K
+        assert gemm_ex_status(K=4096, cfg=c, ws=FAKE, ws_bytes=1 << 30) == NO_CONFIG
+        assert b"no stream-K kernel" in dg.library().dg_last_error()
+    simt = [c for c in dg.candidates(F32, F32) if c.variant == dg.VARIANT_SIMT][0]
+    simt.k_splits = dg.STREAM_K
+    assert gemm_ex_status(K=4096, cfg=simt, dt=F32, out=F32, a=(4096, 1), b=(64, 1), ws=FAKE,
+                          ws_bytes=1 << 30) == NO_CONFIG
+    # never the library's own choice
+    for M, N, K in [(1000, 1500, 777), (4096, 4352, 4096), (5120, 5120, 1024)]:
+        c, _ = dg.select_config_ex(M, N, K, (K, 1), (1, K), (N, 1), BF16, BF16, batch=1, workspace_bytes=1 << 30)
+        assert c.k_splits != dg.STREAM_K, ((M, N, K), c)
 
 
 def test_select_config_never_splits_without_workspace():

@@ -1,6 +1,6 @@
 """GPU parity of the allocation-free entry point dg_gemm_ex_noalloc.
 
-It runs the same kernels as dg_gemm_ex, with split-K partial tiles in the
+It runs the same kernels as dg_gemm_ex, with split-K / stream-K partial tiles in the
 library's fixed per-GPU scratch array instead of a caller workspace. Each case
 calls it through the C-ABI and compares with dg_gemm_ex (given a workspace) on
 the same inputs and config: bit-exact, since both run the same kernels with
@@ -121,3 +121,16 @@ def test_noalloc_rejects_partials_beyond_scratch():
     assert e.value.status == 2 and "scratch" in str(e.value)
     torch.cuda.synchronize()
     assert bool((c == 7.0).all())
+
+
+def test_noalloc_stream_k_two_calls():
+    """Stream-K keeps its flags and partials in the scratch too: a 1000x1496x776
+    product (384 tiles of 64x64, 1.5 rounds), then a smaller 128x128-tile call,
+    bit-exact against dg_gemm_ex and the oracle."""
+    cases = [((1000, 1496, 776), split_config(64, 64, 64, 4, dg.STREAM_K), 31),
+             ((700, 296, 200), split_config(128, 128, 64, 2, dg.STREAM_K), 32)]
+    for (M, N, K), cfg, seed in cases:
+        note(f"noalloc stream-K {M}x{N}x{K} tile={cfg.block_m}x{cfg.block_n}")
+        free, ws, want = run_pair(M, N, K, cfg, seed, epilogue=True)
+        assert np.array_equal(free, ws), f"{M}x{N}x{K}: noalloc differs from dg_gemm_ex"
+        assert np.array_equal(free, want), f"{M}x{N}x{K}: noalloc differs from the oracle"
