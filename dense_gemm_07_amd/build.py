@@ -16,7 +16,7 @@ LIB = os.path.join(LIBDIR, "libdg.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dg_host.cpp", "simt.hip", "split_reduce.hip", "attention.hip"] + [
+SOURCES = ["dg_host.cpp", "simt.hip", "split_reduce.hip", "attention.hip", "mfma_f32.hip"] + [
     f"mfma_{t}_{m}.hip" for t in ("bf16", "f16") for m in ("kc_rc", "kc_kc", "rc_rc", "rc_kc", "gn", "unaligned")]
 
 COMMON = [

@@ -241,6 +241,7 @@ const std::vector<KernelEntry> &registry() {
         register_mfma_f16_rc_kc(r);
         register_mfma_f16_gn(r);
         register_mfma_f16_unaligned(r);
+        register_mfma_f32(r);
         return r;
     }();
     return reg;
@@ -263,7 +264,22 @@ int staged_mode(int64_t rows, int64_t K, int64_t srow, int64_t sk) {
 // 16-byte vector layout: the direct-to-LDS kernel. Otherwise the
 // register-staged kernel: contiguous operands keep 16-byte loads at any
 // alignment; an operand with no unit stride makes both use element loads.
+// fp32 operands on the fp32 matrix-core kernel: 16-byte chunks of 4 floats
+// along k (K % 4 == 0) or along the rows (rows % 4 == 0), else elements.
+int f32_mode(const void *base, int64_t rows, int64_t K, int64_t srow, int64_t sk) {
+    if (!aligned16(base)) return LD_GN;
+    if (sk == 1 && K % 4 == 0 && (rows <= 1 || srow % 4 == 0)) return LD_KC;
+    if (srow == 1 && rows % 4 == 0 && (K <= 1 || sk % 4 == 0)) return LD_RC;
+    return LD_GN;
+}
+
 std::pair<int, int> mfma_modes(const Problem &p) {
+    if (p.in == DG_F32) {
+        const bool a_vec = p.batch <= 1 || p.bsa % 4 == 0;
+        const bool b_vec = p.batch <= 1 || p.bsb % 4 == 0;
+        return {a_vec ? f32_mode(p.A, p.M, p.K, p.sam, p.sak) : LD_GN,
+                b_vec ? f32_mode(p.B, p.N, p.K, p.sbn, p.sbk) : LD_GN};
+    }
     // Every product of a batch starts 16-byte aligned iff the first does and
     // the batch stride is a multiple of 8 elements.
     const bool a_vec = p.batch <= 1 || p.bsa % 8 == 0;
@@ -450,12 +466,19 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
     dg_config best{};
     bool have = false;
     if (p.in == DG_F32) {
-        // fp32 inputs: the scalar kernel, the small tile for tiny problems.
+        // fp32 inputs: tiny problems (C of at most 16 64x64 tiles) take the
+        // scalar kernel's 32x32 tile, whose launch is the shortest; the rest
+        // the fp32 matrix-core kernel, 128x128 when that gives a tile per CU,
+        // else 64x64.
+        const bool small = p.M * p.N <= 64 * 64 * 16;
+        const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
+        const int want = t128 >= cus ? 128 : 64;
         for (const auto &s : shapes) {
-            const bool small = p.M * p.N <= 64 * 64 * 16;
-            if ((small && s.block_m == 32) || (!small && s.block_m == 64)) {
+            if (small ? (s.variant == DG_VARIANT_SIMT && s.block_m == 32)
+                      : (s.variant == DG_VARIANT_MFMA && s.block_m == want && find_kernel(s, p))) {
                 best = s;
                 have = true;
+                break;
             }
         }
     } else {
@@ -524,7 +547,7 @@ std::map<Key, dg_config> g_cache;
 
 Key key_of(const Problem &p) {
     Key k{p.M, p.N, p.K, p.batch, p.in, p.out, -1, -1, c_class(p)};
-    if (p.in != DG_F32) std::tie(k.la, k.lb) = mfma_modes(p);
+    std::tie(k.la, k.lb) = mfma_modes(p);
     return k;
 }
 

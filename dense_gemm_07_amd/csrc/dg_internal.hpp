@@ -85,6 +85,7 @@ struct KernelEntry {
 
 // Registration hooks, one per kernel translation unit.
 void register_simt(std::vector<KernelEntry> &out);
+void register_mfma_f32(std::vector<KernelEntry> &out);
 // The split-K reduction kernel for an MFMA tile shape (nullptr if none).
 LaunchFn split_reduce_kernel(int block_m, int block_n, int waves);
 #define DG_DECLARE_MFMA_HOOKS(t)                               \

@@ -1963,4 +1963,192 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_split_reduce(GemmArgs g) {
     write_tile<BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, w.pm * BM, w.pn * BN);
 }
 
+
+// ============================================================================
+// gemm_mfma_f32: fp32 inputs on the matrix cores (v_mfma_f32_32x32x2_f32)
+// ============================================================================
+// D[32x32] += A[32x2] * B[2x32]: lane l holds A[l % 32][l / 32] and
+// B[l / 32][l % 32] (one fp32 each); the result layout is the 16-bit
+// kernels'. A lane reads four consecutive k of its row from LDS (one
+// ds_read_b128) and feeds them to four successive products: product j of an
+// 8-k group takes k = 4 * (l / 32) + j, for A and B alike, so every k of the
+// group is summed once (the k order within the 32 x 2 products only has to
+// agree between the operands).
+//
+// Operands are staged through registers into LDS tiles [rows][BK + 4], k
+// contiguous (the 4-float pad spreads the rows of a fragment read over the
+// banks). The global loads per load mode:
+//  LD_KC: k stride 1, rows 16-byte aligned, K % 4 == 0: 4-float chunks along
+//         k, one 16-byte load each, written to LDS as they are;
+//  LD_RC: row stride 1, k-lines 16-byte aligned, rows % 4 == 0: 4-float
+//         chunks along the rows, one 16-byte load each, written to LDS as
+//         four floats;
+//  LD_GN: anything else, element loads through both strides.
+// Every load is branch-free: its row and k are clamped into the operand (a
+// chunk is wholly inside or wholly outside the view, given the mode's
+// conditions), and store() writes zeros for what lies outside. A branch
+// around a load would make the compiler wait for it where the paths join.
+// Two register sets keep two slices in flight: slice kt+2 is requested at
+// the top of step kt (slices past K re-read the last one) and written to LDS
+// at the end of step kt+1.
+template <int ROWS, int BK, int T, int MODE>
+struct F32Loader {
+    static_assert(MODE == LD_KC || MODE == LD_RC || MODE == LD_GN, "fp32 load modes");
+    static constexpr int LDK = BK + 4;
+    static constexpr int NCH = ROWS * BK / 4;  // 4-float chunks (KC, RC) per slice
+    static constexpr int PER = MODE == LD_GN ? ROWS * BK / T : NCH / T;
+    static_assert(MODE == LD_GN ? (ROWS * BK) % T == 0 : NCH % T == 0, "chunks split evenly over the threads");
+    static constexpr int NREG = MODE == LD_GN ? PER : PER * 4;
+    float reg[2][NREG];
+    const float *base;  // element (row 0, k = 0) of the tile
+    int64_t srow, sk;
+    int rows_valid, K;  // >= 1 (>= 4 rows for LD_RC), >= 4 for LD_KC
+
+    // The (row, k) of thread chunk c of a slice starting at k0.
+    __device__ static __forceinline__ void chunk(int c, int tid, int k0, int &r, int &k) {
+        const int q = c * T + tid;
+        if constexpr (MODE == LD_KC) r = q / (BK / 4), k = k0 + (q % (BK / 4)) * 4;
+        else if constexpr (MODE == LD_RC) k = k0 + q / (ROWS / 4), r = (q % (ROWS / 4)) * 4;
+        else r = q / BK, k = k0 + q % BK;
+    }
+
+    template <int SET>
+    __device__ __forceinline__ void load(int tid, int k0) {
+#pragma unroll
+        for (int c = 0; c < PER; ++c) {
+            int r, k;
+            chunk(c, tid, k0, r, k);
+            if constexpr (MODE == LD_KC) {
+                const float4 v = *reinterpret_cast<const float4 *>(base + (int64_t)min(r, rows_valid - 1) * srow +
+                                                                  min(k, K - 4));
+                reg[SET][4 * c] = v.x, reg[SET][4 * c + 1] = v.y, reg[SET][4 * c + 2] = v.z, reg[SET][4 * c + 3] = v.w;
+            } else if constexpr (MODE == LD_RC) {
+                const float4 v = *reinterpret_cast<const float4 *>(base + (int64_t)min(k, K - 1) * sk +
+                                                                  min(r, rows_valid - 4));
+                reg[SET][4 * c] = v.x, reg[SET][4 * c + 1] = v.y, reg[SET][4 * c + 2] = v.z, reg[SET][4 * c + 3] = v.w;
+            } else {
+                reg[SET][c] = base[(int64_t)min(r, rows_valid - 1) * srow + (int64_t)min(k, K - 1) * sk];
+            }
+        }
+    }
+
+    template <int SET>
+    __device__ __forceinline__ void store(int tid, int k0, float *lds) const {
+#pragma unroll
+        for (int c = 0; c < PER; ++c) {
+            int r, k;
+            chunk(c, tid, k0, r, k);
+            const bool in = r < rows_valid && k < K;
+            if constexpr (MODE == LD_KC) {
+                *reinterpret_cast<float4 *>(lds + r * LDK + (k - k0)) =
+                    in ? make_float4(reg[SET][4 * c], reg[SET][4 * c + 1], reg[SET][4 * c + 2], reg[SET][4 * c + 3])
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            } else if constexpr (MODE == LD_RC) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lds[(r + e) * LDK + (k - k0)] = in ? reg[SET][4 * c + e] : 0.0f;
+            } else {
+                lds[r * LDK + (k - k0)] = in ? reg[SET][c] : 0.0f;
+            }
+        }
+    }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int LA, int LB, int EM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_f32(GemmArgs g) {
+    constexpr int T = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int LDK = BK + 4;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 8 == 0, "tile shape");
+    constexpr int STAGE = (BM + BN) * LDK;  // floats
+    __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
+
+    const WorkItem w = work_item(blockIdx.x, g);
+    const int m0 = w.pm * BM, n0 = w.pn * BN;
+    const int k_begin = w.split * g.k_chunk;
+    const int kl = min(g.K - k_begin, g.k_chunk);  // this workgroup's K range
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    F32Loader<BM, BK, T, LA> la;
+    F32Loader<BN, BK, T, LB> lb;
+    la.base = static_cast<const float *>(g.A) + (int64_t)w.prod * g.bsa + (int64_t)m0 * g.sam + (int64_t)k_begin * g.sak;
+    la.srow = g.sam;
+    la.sk = g.sak;
+    la.rows_valid = min(BM, g.M - m0);
+    la.K = kl;
+    lb.base = static_cast<const float *>(g.B) + (int64_t)w.prod * g.bsb + (int64_t)n0 * g.sbn + (int64_t)k_begin * g.sbk;
+    lb.srow = g.sbn;
+    lb.sk = g.sbk;
+    lb.rows_valid = min(BN, g.N - n0);
+    lb.K = kl;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = (kl + BK - 1) / BK;
+    // This lane's fragment offsets (floats): row l % 32 of each 32-row block,
+    // k = 4 * (l / 32) within each 8-k group.
+    const int a_off = (wm * WTM + (lane & 31)) * LDK + 4 * (lane >> 5);
+    const int b_off = BM * LDK + (wn * WTN + (lane & 31)) * LDK + 4 * (lane >> 5);
+    auto multiply = [&](const float *s) {
+#pragma unroll
+        for (int kg = 0; kg < BK / 8; ++kg) {
+            float4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const float4 *>(s + a_off + i * 32 * LDK + kg * 8);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const float4 *>(s + b_off + j * 32 * LDK + kg * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const float a = e == 0 ? af[i].x : e == 1 ? af[i].y : e == 2 ? af[i].z : af[i].w;
+                        const float b = e == 0 ? bf[j].x : e == 1 ? bf[j].y : e == 2 ? bf[j].z : bf[j].w;
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i][j], 0, 0, 0);
+                    }
+        }
+    };
+    // Step kt (slice kt in LDS buffer kt & 1, set kt & 1 free): request slice
+    // kt+2 into set kt & 1, multiply, write slice kt+1 (set (kt+1) & 1) into
+    // the other buffer, synchronise. Two steps per iteration keep the set and
+    // buffer indices compile-time.
+    auto step = [&](auto u_tag, int kt) {
+        constexpr int U = decltype(u_tag)::value;
+        la.template load<U>(tid, (kt + 2) * BK);
+        lb.template load<U>(tid, (kt + 2) * BK);
+        multiply(lds + U * STAGE);
+        if (kt + 1 < nk) {
+            la.template store<U ^ 1>(tid, (kt + 1) * BK, lds + (U ^ 1) * STAGE);
+            lb.template store<U ^ 1>(tid, (kt + 1) * BK, lds + (U ^ 1) * STAGE + BM * LDK);
+        }
+        __syncthreads();
+    };
+    if (nk > 0) {
+        la.template load<0>(tid, 0);
+        lb.template load<0>(tid, 0);
+        la.template load<1>(tid, BK);
+        lb.template load<1>(tid, BK);
+        la.template store<0>(tid, 0, lds);
+        lb.template store<0>(tid, 0, lds + BM * LDK);
+        __syncthreads();
+    }
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+        step(std::integral_constant<int, 0>{}, kt);
+        step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+    if (kt < nk) step(std::integral_constant<int, 0>{}, kt);
+
+    finish_tile<EM, BM, BN, WM, WN, FM, FN, (int)sizeof(lds)>(g, w, acc, lds, m0, n0);
+}
+
 }  // namespace dg

@@ -66,7 +66,8 @@ typedef enum dg_status {
 /* Kernel families (dg_config.variant). */
 enum {
     DG_VARIANT_SIMT = 0,  /* LDS-tiled fp32 FMA kernel: any dtype pair, any strides */
-    DG_VARIANT_MFMA = 1   /* fp16/bf16 inputs: v_mfma_f32_32x32x16 tiles, fp32 accumulators */
+    DG_VARIANT_MFMA = 1   /* matrix cores, fp32 accumulators: v_mfma_f32_32x32x16 for fp16/bf16
+                             inputs, v_mfma_f32_32x32x2_f32 for fp32 inputs */
 };
 
 /*

@@ -613,3 +613,45 @@ def test_autotune_ex_caches_and_matches():
     with pytest.raises(dg.DGError):
         dg.autotune_ex(ad, bd, out=torch.zeros(M, N, device=DEV), beta=1.0)
     dg.cache_clear()
+
+
+# ---- fp32 inputs on the matrix cores ------------------------------------------------
+
+def f32_config(bm, splits=1):
+    for c in dg.candidates(dg.DG_F32, dg.DG_F32):
+        if c.variant == dg.VARIANT_MFMA and c.block_m == bm:
+            c.group_m, c.xcd_remap, c.k_splits = 8, 1, splits
+            return c
+    raise LookupError(bm)
+
+
+@pytest.mark.parametrize("layout", ["row/row", "row/col", "col/row", "col/col", "gap/col", "mis/row"])
+def test_fp32_matrix_core_random(layout):
+    """fp32 inputs on v_mfma_f32_32x32x2_f32: the library's choice (64x64 tiles
+    here), the 128x128 tile, split-K and the fused epilogue, random normal
+    inputs, within the fp32 tolerance of the oracle on every load mode
+    (16-byte chunks along k or along the rows, element loads)."""
+    M, N, K = 1032, 900, 1000  # multiples of 4, not of 8: 4-float chunks with M/N edges
+    la, lb = layout.split("/")
+    a, b = inputs.random_operands(M, N, K, "f32", seed=len(layout), dist=("normal", 1.0))
+    ref = ref_product(a, b, "f32")
+    ad, bd = place(a, la), place(b, lb)
+    chosen, _ = dg.select_config(ad, bd, torch.empty(M, N, device=DEV))
+    assert chosen.variant == dg.VARIANT_MFMA, chosen
+    bias = torch.randn(N, generator=torch.Generator().manual_seed(5))
+    for name, cfg in [("default", None), ("128", f32_config(128)), ("split4", f32_config(64, 4))]:
+        for out_dtype in ("f32", "bf16"):
+            what = f"fp32 {layout} {name} -> {out_dtype}"
+            note(what)
+            c = dg.gemm_ex(ad, bd, out_dtype=TD[out_dtype], config=cfg)
+            torch.cuda.synchronize()
+            got = to_f64(c)
+            assert_within_tol(got, ref, epilogue_tolerance(K, "f32", out_dtype, got, ref, 1.0, np.abs(ref), "none"),
+                              what)
+    c = dg.gemm_ex(ad, bd, out_dtype=torch.float32, bias=bias.to(DEV), activation="relu", alpha=0.5)
+    torch.cuda.synchronize()
+    want = oracle.epilogue(ref, alpha=0.5, bias_bits=inputs.bits(bias, "f32"), bias_dtype="f32", act="relu")
+    got = to_f64(c)
+    assert_within_tol(got, want, epilogue_tolerance(K, "f32", "f32", got, want, 0.5,
+                                                    np.abs(0.5 * ref) + np.abs(bias.double().numpy())[None], "relu"),
+                      f"fp32 {layout} epilogue")

@@ -148,6 +148,11 @@ def test_heuristic_choices():
     assert not hit and c.variant == dg.VARIANT_MFMA and (c.block_m, c.block_n) == (256, 256)
     c, _ = dg.select_config_raw(26, 26, 26, (26, 1), (26, 1), (26, 1), F32, F32)
     assert c.variant == dg.VARIANT_SIMT
+    # fp32 beyond tiny sizes: the fp32 matrix-core kernel, 128x128 once that fills the CUs
+    c, _ = dg.select_config_raw(1024, 1024, 1024, (1024, 1), (1024, 1), (1024, 1), F32, F32)
+    assert c.variant == dg.VARIANT_MFMA and (c.block_m, c.block_k) == (64, 32)
+    c, _ = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (4096, 1), (4096, 1), F32, F16)
+    assert c.variant == dg.VARIANT_MFMA and (c.block_m, c.block_k) == (128, 32)
     c, _ = dg.select_config_raw(1024, 1024, 1024, (1024, 1), (1024, 1), (1024, 1), F16, F16)
     assert c.variant == dg.VARIANT_MFMA and (1024 // c.block_m) * (1024 // c.block_n) >= 256
 
@@ -158,7 +163,9 @@ def test_candidates_are_distinct_and_complete():
         assert cands, (i, o)
         keys = {tuple(c.as_dict().values()) for c in cands}
         assert len(keys) == len(cands)
-        if i != F32:
+        if i == F32:
+            assert {c.variant for c in cands} == {dg.VARIANT_SIMT, dg.VARIANT_MFMA}
+        else:
             assert all(c.variant == dg.VARIANT_MFMA for c in cands)
             assert {c.group_m for c in cands} >= {1, 8} and {c.xcd_remap for c in cands} == {0, 1}
 
