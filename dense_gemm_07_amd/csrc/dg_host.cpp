@@ -466,11 +466,12 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
     dg_config best{};
     bool have = false;
     if (p.in == DG_F32) {
-        // fp32 inputs: tiny problems (C of at most 16 64x64 tiles) take the
-        // scalar kernel's 32x32 tile, whose launch is the shortest; the rest
-        // the fp32 matrix-core kernel, 128x128 when that gives a tile per CU,
-        // else 64x64.
-        const bool small = p.M * p.N <= 64 * 64 * 16;
+        // fp32 inputs: the fp32 matrix-core kernel, 128x128 when that gives a
+        // tile per CU, else 64x64 (measured on MI355X: 64x64 beats the scalar
+        // kernel's tiles from 64^3 up, 1.7x at 128^3, 2.2x at 512^3); tiny
+        // problems (C within two 32x32 tiles, e.g. 26^3, where the two tie)
+        // keep the scalar kernel's 32x32 tile.
+        const bool small = p.M * p.N <= 2 * 32 * 32;
         const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * nb;
         const int want = t128 >= cus ? 128 : 64;
         for (const auto &s : shapes) {

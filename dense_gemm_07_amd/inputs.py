@@ -79,6 +79,7 @@ EXTRA = {
         Workload("splitk_128x128x8192_bf16", 128, 128, 8192, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
         Workload("splitk_64x64x65536_bf16", 64, 64, 65536, "bf16", "f32", ("normal", 0.02), ("normal", 0.02)),
         Workload("square_1024_bf16", 1024, 1024, 1024, "bf16", "bf16", ("normal", 0.02), ("normal", 0.02)),
+        Workload("square_4096_f32", 4096, 4096, 4096, "f32", "f32", ("normal", 1.0), ("normal", 1.0)),
         Workload("bmm_1024x1024x128_bf16", 1024, 1024, 128, "bf16", "bf16", ("normal", 1.0), ("normal", 1.0)),
     ]
 }

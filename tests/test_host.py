@@ -148,7 +148,12 @@ def test_heuristic_choices():
     assert not hit and c.variant == dg.VARIANT_MFMA and (c.block_m, c.block_n) == (256, 256)
     c, _ = dg.select_config_raw(26, 26, 26, (26, 1), (26, 1), (26, 1), F32, F32)
     assert c.variant == dg.VARIANT_SIMT
-    # fp32 beyond tiny sizes: the fp32 matrix-core kernel, 128x128 once that fills the CUs
+    # fp32 beyond tiny sizes: the fp32 matrix-core kernel, 128x128 once that fills the CUs;
+    # the boundary is C within two 32x32 tiles
+    c, _ = dg.select_config_raw(32, 64, 64, (64, 1), (64, 1), (64, 1), F32, F32)
+    assert c.variant == dg.VARIANT_SIMT
+    c, _ = dg.select_config_raw(64, 64, 64, (64, 1), (64, 1), (64, 1), F32, F32)
+    assert c.variant == dg.VARIANT_MFMA and (c.block_m, c.block_k) == (64, 32)
     c, _ = dg.select_config_raw(1024, 1024, 1024, (1024, 1), (1024, 1), (1024, 1), F32, F32)
     assert c.variant == dg.VARIANT_MFMA and (c.block_m, c.block_k) == (64, 32)
     c, _ = dg.select_config_raw(4096, 4096, 4096, (4096, 1), (4096, 1), (4096, 1), F32, F16)
