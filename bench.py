@@ -284,7 +284,7 @@ def main():
     ap.add_argument("--misalign-a", action="store_true",
                     help="view A one element past a 16-byte boundary (forces the register-staged kernel)")
     ap.add_argument("--rotate", type=int, default=1, metavar="SETS",
-                    help="cycle the plain product through SETS copies of (A, B, C), so that more than the "
+                    help="cycle the product through SETS copies of (A, B, C), so that more than the "
                          "256 MB Infinity Cache is touched between reuses (cold-cache numbers)")
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch.matmul (the ROCm vendor GEMM) on the same operands, for context")
@@ -395,23 +395,31 @@ def main():
     print(f"# workload {w.name}: config {cfg} (autotune {tune_s:.2f} s)", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
+    # Operand sets the steps cycle through (--rotate: copies of A, B and C, so
+    # that B is not in the Infinity Cache when a product reads it).
+    if args.rotate > 1 and (nb > 1 or args.misalign_a):
+        raise SystemExit("--rotate is for single products with aligned operands")
+    sets = [(a, b, c)] + [(a.clone(), b.clone(), torch.empty_like(c)) for _ in range(args.rotate - 1)]
+    turn = [0]
+
+    def next_set():
+        s = sets[turn[0]]
+        turn[0] = (turn[0] + 1) % len(sets)
+        return s
+
     if explicit is not None and not ex:
         def step():
-            dg.gemm_config(a, b, explicit, out=c, stream=stream)
+            sa, sb, sc = next_set()
+            dg.gemm_config(sa, sb, explicit, out=sc, stream=stream)
     elif ex:
         def step():
-            dg.gemm_ex(a, b, out=c, stream=stream, workspace=True if args.split_k else None, config=explicit, **epi)
-    elif args.rotate > 1:  # plain product only
-        sets = [(a, b, c)] + [(a.clone(), b.clone(), torch.empty_like(c)) for _ in range(args.rotate - 1)]
-        turn = [0]
-
-        def step():
-            sa, sb, sc = sets[turn[0]]
-            turn[0] = (turn[0] + 1) % len(sets)
-            dg.gemm(sa, sb, out=sc, stream=stream)
+            sa, sb, sc = next_set()
+            dg.gemm_ex(sa, sb, out=sc, stream=stream, workspace=True if args.split_k else None, config=explicit,
+                       **epi)
     else:
         def step():
-            dg.gemm(a, b, out=c, stream=stream)
+            sa, sb, sc = next_set()
+            dg.gemm(sa, sb, out=sc, stream=stream)
     settle_steps = warm_up(step, args.warmup, args.settle_ms)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -469,7 +477,7 @@ def main():
         "launch_us": launch_us,
         "settle": {"ms": args.settle_ms, "extra_warmup_steps": settle_steps},
     }
-    if args.rotate > 1 and explicit is None and not ex:  # the plain product is the one rotated
+    if args.rotate > 1:
         result["config"]["rotate_sets"] = args.rotate
         result["roofline"]["traffic"] = None
     if ex:
