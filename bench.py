@@ -11,6 +11,7 @@ one-time cost, reported separately). Prints one JSON line.
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -35,15 +36,20 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, cfg):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
+    on the current kernel source and on the tile shape cfg runs; else None."""
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    # The recorded kernel's tile: the first three integer template arguments
+    # (gemm_simt names its two dtypes first, the MFMA kernels one).
+    m = re.search(r"dg::\w+<(?:dg::\w+, )+(\d+), (\d+), (\d+)", (rec.get("kernels") or [""])[0])
+    if not m or tuple(int(x) for x in m.groups()) != (cfg.block_m, cfg.block_n, cfg.block_k):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -447,7 +453,7 @@ def main():
     nbytes = w.compulsory_bytes() * nb + extra_bytes
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.in_dtype]
-    traffic = measured_traffic(w.name) if not ex else None
+    traffic = measured_traffic(w.name, cfg) if not ex else None
     hbm_bound = flops / nbytes < peak * 1e12 / (HBM_GBPS * 1e9)
     if hbm_bound:  # below the ridge: algorithmic bytes over time against the HBM peak
         gbps = nbytes / (ms * 1e-3) / 1e9

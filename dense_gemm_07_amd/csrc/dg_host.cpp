@@ -506,6 +506,23 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
         }
     }
     if (!have && !shapes.empty()) best = shapes.front();
+    // Register-staged 64x64 tiles with both operands k-contiguous off
+    // alignment: BK 32 when BK 64 would pad K by more than 5 % (its last
+    // slice mostly zeros) and BK 32 pads less. Measured on MI355X:
+    // 1000x1500x777 12.5-12.8 against 13.3-13.7 us, 512x512x777 8.50 against
+    // 8.96; where BK 64 pads little (2000x3000x1555, 2.8 %) BK 32 is 11 %
+    // slower, and with a row-contiguous operand it is slower at any K.
+    if (best.variant == DG_VARIANT_MFMA && best.block_m == 64 && best.block_n == 64 && best.block_k == 64 &&
+        p.in != DG_F32 && p.K > 0) {
+        const auto modes = mfma_modes(p);
+        const int64_t k64 = (p.K + 63) / 64 * 64, k32 = (p.K + 31) / 32 * 32;
+        if (modes.first == LD_KU && modes.second == LD_KU && (k64 - p.K) * 20 > k64 && k32 < k64) {
+            dg_config c = best;
+            c.block_k = 32;
+            c.stages = 2;
+            if (find_kernel(c, p)) best = c;
+        }
+    }
     best.group_m = 8;
     best.xcd_remap = 1;
     best.k_splits = 1;

@@ -8,6 +8,7 @@ import sys
 import pytest
 
 import bench
+import dense_gemm_07_amd as dg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -78,12 +79,21 @@ def test_record_traffic_scales_each_counter_by_the_copy(tmp_path, monkeypatch):
     assert rec["kernel_source_hash"] == bench.kernel_source_hash()
 
 
+def tile(bm, bn, bk):
+    c = dg.Config()
+    c.block_m, c.block_n, c.block_k = bm, bn, bk
+    return c
+
+
 def test_traffic_is_reported_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
     rec = recorded(tmp_path, monkeypatch)
-    assert bench.measured_traffic("toy") == rec["hbm_bytes_per_launch"]
-    assert bench.measured_traffic("no_such_workload") is None
+    assert bench.measured_traffic("toy", tile(256, 256, 64)) == rec["hbm_bytes_per_launch"]
+    assert bench.measured_traffic("no_such_workload", tile(256, 256, 64)) is None
+    # ... and only for the tile shape it was taken on
+    assert bench.measured_traffic("toy", tile(256, 256, 32)) is None
+    assert bench.measured_traffic("toy", tile(128, 256, 64)) is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
-    assert bench.measured_traffic("toy") is None
+    assert bench.measured_traffic("toy", tile(256, 256, 64)) is None
 
 
 def test_counter_without_samples_is_an_error(tmp_path):

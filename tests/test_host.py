@@ -162,6 +162,21 @@ def test_heuristic_choices():
     assert c.variant == dg.VARIANT_MFMA and (1024 // c.block_m) * (1024 // c.block_n) >= 256
 
 
+def test_heuristic_bk32_for_short_unaligned_k():
+    # both operands k-contiguous off 16-byte alignment (leading dimension 777
+    # or 1555): BK 32 when BK 64 pads K by more than 5 %
+    c, _ = dg.select_config_raw(1000, 1500, 777, (777, 1), (1, 777), (1500, 1), BF16, dg.DG_F32)
+    assert (c.variant, c.block_m, c.block_n, c.block_k) == (dg.VARIANT_MFMA, 64, 64, 32), c
+    c, _ = dg.select_config_raw(2000, 3000, 1555, (1555, 1), (1, 1555), (3000, 1), BF16, dg.DG_F32)
+    assert c.block_k == 64, c
+    # a row-contiguous B at the same K keeps BK 64
+    c, _ = dg.select_config_raw(1000, 1500, 777, (777, 1), (1500, 1), (1500, 1), BF16, dg.DG_F32)
+    assert c.block_k == 64, c
+    # aligned operands (direct kernel) keep BK 64
+    c, _ = dg.select_config_raw(1000, 1504, 776, (776, 1), (1, 776), (1504, 1), BF16, dg.DG_F32)
+    assert c.block_k == 64, c
+
+
 def test_candidates_are_distinct_and_complete():
     for i, o in itertools.product([F32, F16, BF16], repeat=2):
         cands = dg.candidates(i, o)
