@@ -285,6 +285,20 @@ __device__ __forceinline__ u32x4 drop_elems(u32x4 v, int sh) {
 //  LD_KU: k stride 1. Whole 8-element chunks are one 16-byte load at any
 //         element alignment; a chunk cut by K is loaded element by element.
 //  LD_GN: anything else, element loads through both strides.
+// Element offset of (row, k), k a multiple of 8, in the register kernel's LDS
+// tile. BK 64: rows of LDK = BK + 8 elements (the 16-byte pad breaks the bank
+// pattern of 128-byte rows). BK 32: unpadded 64-byte rows whose four 16-byte
+// chunks are permuted by bits 2-3 of the row, so both the 16-byte writes (a
+// 16-lane group covers 4 rows x 4 chunks) and the fragment reads (16 rows,
+// one chunk) touch 64 distinct banks; the padded 80-byte rows put the writes
+// of rows 0 and 3 on the same banks (measured on MI355X: 614 k conflict
+// cycles of 1.84 M LDS cycles on the 1000x1500x777 product).
+template <int BK, int LDK>
+__device__ __forceinline__ int reg_lds_off(int row, int k) {
+    if constexpr (BK == 32) return row * 32 + ((((k >> 3) ^ (row >> 2)) & 3) << 3);
+    else return row * LDK + k;
+}
+
 template <int ROWS, int BK, int LDK, int T, int MODE>
 struct TileLoader {
     // Row-contiguous unaligned operands (LD_RU) take the staged kernel at
@@ -362,7 +376,7 @@ struct TileLoader {
                 const int r = q / KCH, kc = q % KCH;
                 u32x4 v = reg[c];
                 if constexpr (MODE == LD_KU) v = okc[c] ? v : u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = v;
+                *reinterpret_cast<u32x4 *>(lds + reg_lds_off<BK, LDK>(r, kc * 8)) = v;
             }
         }
     }
@@ -419,7 +433,7 @@ struct KuStream {
                     v = drop_elems(v, k - min(k, kmax));
                 }
                 if (r >= rows_valid) v = u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(lds + r * LDK + kc * 8) = v;
+                *reinterpret_cast<u32x4 *>(lds + reg_lds_off<BK, LDK>(r, kc * 8)) = v;
             }
         }
     }
@@ -1035,9 +1049,10 @@ __device__ __forceinline__ void mfma_reg_tile(const GemmArgs &g, const WorkItem 
     constexpr int T = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int LDK = BK + 8;
+    constexpr int LDK = BK == 32 ? 32 : BK + 8;  // row pitch (elements), see reg_lds_off
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "8-row blocks");
+    static_assert(BK == 32 || BK == 64, "reg_lds_off layouts");
 
     const int m0 = w.pm * BM, n0 = w.pn * BN;
     const int tid = threadIdx.x;
@@ -1105,9 +1120,21 @@ __device__ __forceinline__ void mfma_reg_tile(const GemmArgs &g, const WorkItem 
         __syncthreads();
     }
 
-    // LDS offsets (elements) of this lane's fragment rows.
-    const int a_row = (wm * WTM + (lane & 31)) * LDK + (lane >> 5) * 8;
-    const int b_row = (BM + wn * WTN + (lane & 31)) * LDK + (lane >> 5) * 8;
+    // LDS offsets (elements) of this lane's fragment rows. BK 32: the row
+    // part, and the permuted chunk of each k-substep (bits 2-3 of the row do
+    // not change from one 32-row block to the next).
+    const int a_row = (wm * WTM + (lane & 31)) * LDK + (BK == 32 ? 0 : (lane >> 5) * 8);
+    const int b_row = (BM + wn * WTN + (lane & 31)) * LDK + (BK == 32 ? 0 : (lane >> 5) * 8);
+    int a_ch[2] = {0, 0}, b_ch[2] = {0, 0};
+    if constexpr (BK == 32) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            a_ch[kk] = reg_lds_off<BK, LDK>(wm * WTM + (lane & 31), (lane >> 5) * 8 + 16 * kk) -
+                       (wm * WTM + (lane & 31)) * LDK;
+            b_ch[kk] = reg_lds_off<BK, LDK>(BM + wn * WTN + (lane & 31), (lane >> 5) * 8 + 16 * kk) -
+                       (BM + wn * WTN + (lane & 31)) * LDK;
+        }
+    }
 
     // Step kt: request slice kt+P-1 into set (kt+P-1) % P, multiply slice kt
     // (LDS buffer kt & 1), write slice kt+1 from set (kt+1) % P into the other
@@ -1120,9 +1147,11 @@ __device__ __forceinline__ void mfma_reg_tile(const GemmArgs &g, const WorkItem 
         for (int kk = 0; kk < BK / 16; ++kk) {
             u32x4 af[FM], bf[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(s + a_row + i * 32 * LDK + kk * 16);
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(s + a_row + i * 32 * LDK + (BK == 32 ? a_ch[kk] : kk * 16));
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(s + b_row + j * 32 * LDK + kk * 16);
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const u32x4 *>(s + b_row + j * 32 * LDK + (BK == 32 ? b_ch[kk] : kk * 16));
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
