@@ -234,20 +234,28 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) issue(lds + s * STAGE, s * BKV);
     int cur = 0;
-    for (int kb = 0; kb < nkv; ++kb) {
+    // Block kb: wait for it, synchronise, queue block kb+S-1, then compute.
+    auto step = [&](auto mask_tag, int kb) {
         wait_vmcnt<(S - 2) * LOADS>();  // block kb has landed (this wave's loads)
         stage_barrier();                // ... everyone's; and everyone is done with block kb-1
         const int fill = cur == 0 ? S - 1 : cur - 1;
         issue(lds + fill * STAGE, (kb + S - 1) * BKV);
         const int kv0 = kb * BKV;
         const char *kt = lds + cur * STAGE;
-        if (!CAUSAL || kv0 <= last_q) {
-            const bool mask = kv0 + BKV > a.seq_kv || (CAUSAL && kv0 + BKV - 1 > wq0);
-            if (mask) block(std::true_type{}, kt, kt + K_BYTES, kv0);
-            else block(std::false_type{}, kt, kt + K_BYTES, kv0);
-        }
+        if (!CAUSAL || kv0 <= last_q) block(mask_tag, kt, kt + K_BYTES, kv0);
         cur = cur + 1 == S ? 0 : cur + 1;
-    }
+    };
+    // The blocks that need no mask (every key inside seq_kv and, causal, at
+    // or before this wave's first query) come first, in a loop of their own:
+    // with a single path through the loop, O stays in the same registers
+    // from one block to the next (a masked and an unmasked path joining in
+    // one loop made the compiler copy O between register sets every block).
+    // Every wave runs one iteration, and one barrier, per block; the waves
+    // of a workgroup only differ in which loop an iteration belongs to.
+    const int nfree = min(nkv, (CAUSAL ? min(a.seq_kv, wq0 + 1) : a.seq_kv) / BKV);
+    int kb = 0;
+    for (; kb < nfree; ++kb) step(std::false_type{}, kb);
+    for (; kb < nkv; ++kb) step(std::true_type{}, kb);
     wait_vmcnt<0>();  // the trailing out-of-range loads land before the workgroup exits
 
     // O = O^T / l (lane l holds query my_q[g], head_dim rows 32db + 8*(r/4) + 4*(l/32) + r%4)
