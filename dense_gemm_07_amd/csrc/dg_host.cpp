@@ -300,6 +300,13 @@ std::pair<int, int> mfma_modes(const Problem &p) {
 
 bool register_staged(int la) { return la == LD_KU || la == LD_RU || la == LD_GN; }
 
+// Both operands of a 16-bit problem in the direct-to-LDS kernel's layouts.
+bool direct_modes(const Problem &p) {
+    if (p.in == DG_F32) return false;
+    const auto m = mfma_modes(p);
+    return (m.first == LD_KC || m.first == LD_RC) && (m.second == LD_KC || m.second == LD_RC);
+}
+
 // The register-staged MFMA kernel always double-buffers: for a problem that
 // needs it, a config's `stages` is not part of the match.
 const KernelEntry *find_kernel(const dg_config &cfg, const Problem &p) {
@@ -480,6 +487,35 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
                 best = s;
                 have = true;
                 break;
+            }
+        }
+    } else if (direct_modes(p)) {
+        // Both operands in the direct kernel's layouts: the tile shape with the
+        // least estimated time, rounds x work per workgroup / its rate, where a
+        // round is one workgroup per slot (CUs x workgroups that fit per CU)
+        // and the rates are per CU, relative to the 256x256 tile. Fitted to
+        // kernel traces on MI355X (bf16, 1536^3 to 5120^3): at 3584^3 the
+        // 196 tiles of 256x256 took 77 us, 256x128 107 (two rounds), 128x128
+        // at two stages 96 (two per CU), at three stages 116, 64x64 141. A
+        // tile count just past a round costs a whole round, so "the biggest
+        // tile that still fills the CUs" lost up to 39 % (3072^3: 256x128,
+        // 288 tiles, 92 us, against 256x256, 144 tiles, 56 us).
+        struct Cand { int bm, bn, bk, waves, stages, per_cu; double rate; };
+        static const Cand kCands[] = {
+            {256, 256, 64, 8, 2, 1, 1.00}, {128, 256, 64, 4, 2, 1, 0.72}, {256, 128, 64, 4, 2, 1, 0.72},
+            {128, 128, 64, 4, 3, 1, 0.67}, {128, 128, 64, 4, 2, 2, 0.80}, {64, 64, 64, 4, 4, 2, 0.48},
+        };
+        double best_t = 0.0;
+        for (const Cand &c : kCands) {
+            dg_config s{c.bm, c.bn, c.bk, 1, c.waves, c.stages, DG_VARIANT_MFMA, 0, 1};
+            if (!find_kernel(s, p)) continue;
+            const int64_t tiles = ((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn) * nb;
+            const int64_t slots = (int64_t)cus * c.per_cu;
+            const double t = (double)((tiles + slots - 1) / slots) * (c.bm * c.bn / 65536.0) * c.per_cu / c.rate;
+            if (!have || t < best_t) {
+                best = s;
+                best_t = t;
+                have = true;
             }
         }
     } else {

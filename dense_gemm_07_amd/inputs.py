@@ -10,6 +10,7 @@ torch's round-to-nearest-even cast. uniform[-1, 1) is `2*rand - 1`;
 N(0, s) is `s * randn`. A column-major B is drawn as its row-major storage
 [N, K] and handed out as the transposed view (strides (1, K)).
 """
+import re
 from dataclasses import dataclass
 
 import numpy as np
@@ -86,10 +87,17 @@ EXTRA = {
 
 
 def find(name: str) -> Workload:
-    """A workload by name from any of the tables."""
+    """A workload by name from any of the tables, or a plain product named
+    gemm_<M>x<N>x<K>_<dtype> (row-major operands from N(0, 0.02), output in
+    the input dtype), for measurements across sizes."""
     for table in (WORKLOADS, SKINNY, EXTRA):
         if name in table:
             return table[name]
+    m = re.fullmatch(r"gemm_(\d+)x(\d+)x(\d+)_(bf16|f16|f32)", name)
+    if m:
+        M, N, K = (int(x) for x in m.groups()[:3])
+        dt = m.group(4)
+        return Workload(name, M, N, K, dt, dt, ("normal", 0.02), ("normal", 0.02))
     raise KeyError(f"unknown workload {name!r}")
 
 

@@ -100,3 +100,13 @@ def test_counter_without_samples_is_an_error(tmp_path):
     empty = counters(tmp_path, "e.csv", [(COPY, "WRITE_SIZE", 1.0)])
     with pytest.raises(SystemExit):
         bench._counter_median(empty, "FETCH_SIZE", "dg::gemm")
+
+
+def test_sized_workload_names():
+    from dense_gemm_07_amd import inputs
+    w = inputs.find("gemm_2048x1024x512_f16")
+    assert (w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_colmajor) == (2048, 1024, 512, "f16", "f16", False)
+    assert inputs.find("square_4096_bf16").M == 4096  # the tables come first
+    for bad in ("gemm_2048x1024_bf16", "gemm_1x2x3_int8", "gemm_axbxc_bf16"):
+        with pytest.raises(KeyError):
+            inputs.find(bad)

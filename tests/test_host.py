@@ -162,6 +162,20 @@ def test_heuristic_choices():
     assert c.variant == dg.VARIANT_MFMA and (1024 // c.block_m) * (1024 // c.block_n) >= 256
 
 
+def test_heuristic_counts_rounds_of_tiles():
+    # aligned bf16 squares: the tile shape with the least rounds x work per
+    # workgroup / rate, not the biggest tile that fills the CUs
+    want = {1536: (128, 128, 3), 2048: (128, 128, 3), 2560: (128, 128, 2), 3072: (256, 256, 2),
+            3584: (256, 256, 2), 4096: (256, 256, 2), 6144: (256, 256, 2), 1024: (64, 64, 4)}
+    for n, (bm, bn, st) in want.items():
+        c, _ = dg.select_config_raw(n, n, n, (n, 1), (n, 1), (n, 1), BF16, BF16)
+        assert (c.block_m, c.block_n, c.stages) == (bm, bn, st), (n, c)
+    c, _ = dg.select_config_raw(8192, 14336, 4096, (4096, 1), (14336, 1), (14336, 1), BF16, BF16)
+    assert (c.block_m, c.block_n) == (256, 256), c
+    c, _ = dg.select_config_raw(16, 14336, 4096, (4096, 1), (14336, 1), (14336, 1), BF16, BF16)
+    assert (c.block_m, c.block_n) == (64, 64), c
+
+
 def test_heuristic_bk32_for_short_unaligned_k():
     # both operands k-contiguous off 16-byte alignment (leading dimension 777
     # or 1555): BK 32 when BK 64 pads K by more than 5 %
