@@ -307,6 +307,14 @@ bool direct_modes(const Problem &p) {
     return (m.first == LD_KC || m.first == LD_RC) && (m.second == LD_KC || m.second == LD_RC);
 }
 
+// Both operands of a 16-bit problem contiguous but off 16-byte alignment
+// (the register-staged kernels' 16-byte loads).
+bool staged_modes(const Problem &p) {
+    if (p.in == DG_F32) return false;
+    const auto m = mfma_modes(p);
+    return (m.first == LD_KU || m.first == LD_RU) && (m.second == LD_KU || m.second == LD_RU);
+}
+
 // The register-staged MFMA kernel always double-buffers: for a problem that
 // needs it, a config's `stages` is not part of the match.
 const KernelEntry *find_kernel(const dg_config &cfg, const Problem &p) {
@@ -489,24 +497,36 @@ dg_config heuristic(const Problem &p, int cus, int64_t ws_bytes) {
                 break;
             }
         }
-    } else if (direct_modes(p)) {
-        // Both operands in the direct kernel's layouts: the tile shape with the
-        // least estimated time, rounds x work per workgroup / its rate, where a
-        // round is one workgroup per slot (CUs x workgroups that fit per CU)
-        // and the rates are per CU, relative to the 256x256 tile. Fitted to
-        // kernel traces on MI355X (bf16, 1536^3 to 5120^3): at 3584^3 the
-        // 196 tiles of 256x256 took 77 us, 256x128 107 (two rounds), 128x128
-        // at two stages 96 (two per CU), at three stages 116, 64x64 141. A
-        // tile count just past a round costs a whole round, so "the biggest
-        // tile that still fills the CUs" lost up to 39 % (3072^3: 256x128,
-        // 288 tiles, 92 us, against 256x256, 144 tiles, 56 us).
+    } else if (direct_modes(p) || staged_modes(p)) {
+        // The tile shape with the least estimated time, rounds x work per
+        // workgroup / its rate. A round is one workgroup per slot (CUs x
+        // workgroups that fit per CU); the rates are per CU, relative to the
+        // 256x256 tile, fitted to kernel traces on MI355X (bf16, 1536^3 to
+        // 5120^3). Direct kernel, at 3584^3: the 196 tiles of 256x256 took
+        // 77 us, 256x128 107 (two rounds), 128x128 at two stages 96 (two per
+        // CU), at three stages 116, 64x64 141. Register-staged kernel (A one
+        // element off alignment), at 3584^3: 256x256 110 us, 256x128 196,
+        // 128x128 229, 64x64 229. A tile count just past a round costs a
+        // whole round, so "the biggest tile that still fills the CUs" lost
+        // up to 45 % (3072^3 staged: 256x128, 288 tiles, 169 us, against
+        // 256x256, 144 tiles, 94 us). Problems whose operands need element
+        // loads keep the rule below.
         struct Cand { int bm, bn, bk, waves, stages, per_cu; double rate; };
-        static const Cand kCands[] = {
+        static const Cand kDirect[] = {
             {256, 256, 64, 8, 2, 1, 1.00}, {128, 256, 64, 4, 2, 1, 0.72}, {256, 128, 64, 4, 2, 1, 0.72},
             {128, 128, 64, 4, 3, 1, 0.67}, {128, 128, 64, 4, 2, 2, 0.80}, {64, 64, 64, 4, 4, 2, 0.48},
         };
+        // (the staged kernels take any stage count: one entry per tile)
+        static const Cand kStaged[] = {
+            {256, 256, 64, 8, 2, 1, 1.00}, {128, 256, 64, 4, 2, 1, 0.56}, {256, 128, 64, 4, 2, 1, 0.56},
+            {128, 128, 64, 4, 2, 1, 0.48}, {64, 64, 64, 4, 2, 2, 0.42},
+        };
+        const bool direct = direct_modes(p);
+        const Cand *cands = direct ? kDirect : kStaged;
+        const int ncand = direct ? (int)(sizeof(kDirect) / sizeof(Cand)) : (int)(sizeof(kStaged) / sizeof(Cand));
         double best_t = 0.0;
-        for (const Cand &c : kCands) {
+        for (int i = 0; i < ncand; ++i) {
+            const Cand &c = cands[i];
             dg_config s{c.bm, c.bn, c.bk, 1, c.waves, c.stages, DG_VARIANT_MFMA, 0, 1};
             if (!find_kernel(s, p)) continue;
             const int64_t tiles = ((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn) * nb;

@@ -176,6 +176,16 @@ def test_heuristic_counts_rounds_of_tiles():
     assert (c.block_m, c.block_n) == (64, 64), c
 
 
+def test_heuristic_counts_rounds_for_staged_operands():
+    # A off 16-byte alignment (base address 2 bytes past a boundary): the
+    # register-staged kernels' rates in the same round-counting model
+    want = {1536: (128, 128), 2560: (128, 256), 3072: (256, 256), 3584: (256, 256), 4096: (256, 256)}
+    for n, tile in want.items():
+        c, _ = dg.select_config_raw(n, n, n, (n, 1), (n, 1), (n, 1), BF16, BF16, ptr_a=0x1002, ptr_b=0x2000,
+                                    ptr_c=0x3000)
+        assert (c.block_m, c.block_n) == tile, (n, c)
+
+
 def test_heuristic_bk32_for_short_unaligned_k():
     # both operands k-contiguous off 16-byte alignment (leading dimension 777
     # or 1555): BK 32 when BK 64 pads K by more than 5 %
