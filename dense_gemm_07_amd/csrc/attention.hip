@@ -39,6 +39,16 @@ namespace dg {
 // LDS row i of a K block holds key i with bits 2 and 3 swapped (an involution).
 __device__ __forceinline__ int attn_key_of_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
+// c * max(x of lane l, x of lane l ^ 32) in every lane, for c > 0: gfx950
+// swaps the upper half of one register with the lower half of another in one
+// VALU instruction, which spares a round trip through LDS. Scaling each half
+// first gives the same value (rounding is monotone) and spares the moves that
+// fmaxf needs on values of unknown origin.
+__device__ __forceinline__ float scaled_max_of_halves(float x, float c) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]) * c, __uint_as_float(r[1]) * c);
+}
+
 template <typename TI, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     constexpr int NW = 4;
@@ -109,17 +119,19 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         vkey[j] = k;
         vvo[j] = (int)(2 * ((int64_t)k * a.vs + row));
     }
-    // Queue key block [kv0, kv0 + BKV) into `stage`; keys past seq_kv load zeros.
-    auto issue = [&](char *stage, int kv0) {
+    // Queue key block [kv0, kv0 + BKV) into `stage`; with CHECK, keys past
+    // seq_kv load zeros (without, the caller knows the block lies inside).
+    auto issue = [&](auto check_tag, char *stage, int kv0) {
+        constexpr bool CHECK = decltype(check_tag)::value;
 #pragma unroll
         for (int j = 0; j < K_PER; ++j) {
-            const int vo = kv0 + kkey[j] < a.seq_kv ? kvo[j] : kOobOffset;
+            const int vo = !CHECK || kv0 + kkey[j] < a.seq_kv ? kvo[j] : kOobOffset;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t *)(stage + (wave + NW * j) * 1024), 16, vo,
                                                      (int)(2 * (int64_t)kv0 * a.ks), 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < V_PER; ++j) {
-            const int vo = kv0 + vkey[j] < a.seq_kv ? vvo[j] : kOobOffset;
+            const int vo = !CHECK || kv0 + vkey[j] < a.seq_kv ? vvo[j] : kOobOffset;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t *)(stage + K_BYTES + (wave + NW * j) * 1024),
                                                      16, vo, (int)(2 * (int64_t)kv0 * a.vs), 0, 0);
         }
@@ -135,9 +147,12 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[g][db][r] = 0.0f;
-    float m[QG], l[QG];  // running max of the log2-scaled scores; this lane's running sum (its half of the keys)
+    // m: the reference max of the log2-scaled scores (-inf until a key is
+    // allowed); nmu: -m, or 0 while m is -inf (the weights then stay 0);
+    // l: this lane's running sum (its half of the keys).
+    float m[QG], nmu[QG], l[QG];
 #pragma unroll
-    for (int g = 0; g < QG; ++g) m[g] = -__builtin_inff(), l[g] = 0.0f;
+    for (int g = 0; g < QG; ++g) m[g] = -__builtin_inff(), nmu[g] = 0.0f, l[g] = 0.0f;
 
     // Scores of one key block: S^T = K Q^T for the wave's query groups.
     auto qk = [&](const char *__restrict__ kt, f32x16 (&s)[QG][SB]) {
@@ -177,33 +192,40 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
                     }
                     mb = fmaxf(mb, s[g][sb][r]);
                 }
-            mb = fmaxf(mb, __shfl_xor(mb, 32)) * a.scale_log2;
-            const float mn = fmaxf(m[g], mb);
-            const float mu = mn == -__builtin_inff() ? 0.0f : mn;  // nothing allowed yet: weights stay 0
-            float ps = 0.0f;
+            mb = scaled_max_of_halves(mb, a.scale_log2);
+            // The reference max moves only when some lane's block max exceeds
+            // it by more than 2^kAttnSlack (a wave vote); below that the
+            // weights exp2(x - m) stay under 2^kAttnSlack, and O, l and lse
+            // are relative to the same reference, so the result is the same
+            // up to rounding. With random scores the max stops growing by
+            // that much after the first blocks, so the rescaling of O is
+            // skipped from then on.
+            if (__any(mb > m[g] + kAttnSlack)) {
+                const float mn = fmaxf(m[g], mb);
+                const float nmun = mn == -__builtin_inff() ? 0.0f : -mn;
+                const float alpha = __builtin_amdgcn_exp2f(m[g] + nmun);  // 0 while m is -inf
+                l[g] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[g][db][r] *= alpha;
+                m[g] = mn;
+                nmu[g] = nmun;
+            }
+            float ps = -0.0f;  // -0 + p is p: the first addition folds away
 #pragma unroll
             for (int t = 0; t < PT; ++t) {
                 uint16_t e8[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float p =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][t >> 1][8 * (t & 1) + e], a.scale_log2, -mu));
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][t >> 1][8 * (t & 1) + e], a.scale_log2, nmu[g]));
                     ps += p;
                     e8[e] = from_f32<TI>(p);
                 }
                 pf[g][t] = pack8(e8);
             }
-            // Rescale what was accumulated only when some lane's max grew.
-            if (__any(mn != m[g])) {
-                const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
-                l[g] *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[g][db][r] *= alpha;
-            }
             l[g] += ps;
-            m[g] = mn;
         }
 #pragma unroll
         for (int t = 0; t < PT; ++t)
@@ -232,14 +254,14 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // the compiler from waiting on those loads before reading these).
     const int last_q = wq0 + 32 * QG - 1;  // causal: blocks past it add nothing for this wave
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) issue(lds + s * STAGE, s * BKV);
+    for (int s = 0; s < S - 1; ++s) issue(std::true_type{}, lds + s * STAGE, s * BKV);
     int cur = 0;
     // Block kb: wait for it, synchronise, queue block kb+S-1, then compute.
     auto step = [&](auto mask_tag, int kb) {
         wait_vmcnt<(S - 2) * LOADS>();  // block kb has landed (this wave's loads)
         stage_barrier();                // ... everyone's; and everyone is done with block kb-1
         const int fill = cur == 0 ? S - 1 : cur - 1;
-        issue(lds + fill * STAGE, (kb + S - 1) * BKV);
+        issue(std::true_type{}, lds + fill * STAGE, (kb + S - 1) * BKV);
         const int kv0 = kb * BKV;
         const char *kt = lds + cur * STAGE;
         if (!CAUSAL || kv0 <= last_q) block(mask_tag, kt, kt + K_BYTES, kv0);
@@ -260,17 +282,19 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // At head_dim 128 the compiler moved the unrolled loop's arrays to
     // scratch memory (704 bytes per lane, 25x slower), so it keeps the plain
     // loop.
+    // The block it queues lies inside seq_kv (the loop's condition), so its
+    // loads skip the key test.
     auto step_at = [&](auto u_tag, int kb) {
         constexpr int U = decltype(u_tag)::value;
         wait_vmcnt<(S - 2) * LOADS>();
         stage_barrier();
-        issue(lds + ((U + S - 1) % S) * STAGE, (kb + S - 1) * BKV);
+        issue(std::false_type{}, lds + ((U + S - 1) % S) * STAGE, (kb + S - 1) * BKV);
         const int kv0 = kb * BKV;
         if (!CAUSAL || kv0 <= last_q) block(std::false_type{}, lds + U * STAGE, lds + U * STAGE + K_BYTES, kv0);
     };
     if constexpr (D == 64) {
         static_assert(S == 3, "the unrolled loop covers three stages");
-        for (; kb + S <= nfree; kb += S) {
+        for (; kb + S <= nfree && (kb + 2 * S - 1) * BKV <= a.seq_kv; kb += S) {
             step_at(std::integral_constant<int, 0>{}, kb);
             step_at(std::integral_constant<int, 1>{}, kb + 1);
             step_at(std::integral_constant<int, 2>{}, kb + 2);
