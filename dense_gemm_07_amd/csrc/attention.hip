@@ -28,7 +28,10 @@
 // Numerics: fp32 scores and accumulators; exponentials through exp2 of the
 // scores scaled by scale * log2(e); P is rounded to the input type for the
 // second product (the matrix cores take 16-bit operands), the running sum
-// adds the unrounded fp32 weights.
+// adds the unrounded fp32 weights. The maximum subtracted in the exponent is
+// a reference that moves only when a block's weights against it would grow
+// large (their sum past 2^8): the page's rescaling runs then, not on every
+// growth of the maximum, which gives the same result up to rounding.
 #include <type_traits>
 
 #include "attention.hpp"
@@ -47,6 +50,28 @@ __device__ __forceinline__ int attn_key_of_row(int i) { return (i & ~12) | ((i &
 __device__ __forceinline__ float scaled_max_of_halves(float x, float c) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]) * c, __uint_as_float(r[1]) * c);
+}
+
+// One lane's weights of a key block, exp2(c * s + nm) for its 16 * SB
+// scores, rounded to the input type and packed as the B operands of the
+// product with V (register 8t + e of the scores is key e of 16-key step t),
+// and their sum in fp32. The scale folds into the exponent's fused
+// multiply-add.
+template <typename TI, int SB>
+__device__ __forceinline__ float attn_weights(const f32x16 (&s)[SB], u32x4 (&pf)[2 * SB], float c, float nm) {
+    float ps = -0.0f;  // -0 + p is p: the first addition folds away
+#pragma unroll
+    for (int t = 0; t < 2 * SB; ++t) {
+        uint16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][8 * (t & 1) + e], c, nm));
+            ps += p;
+            e8[e] = from_f32<TI>(p);
+        }
+        pf[t] = pack8(e8);
+    }
+    return ps;
 }
 
 template <typename TI, int D, bool CAUSAL>
@@ -119,9 +144,13 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         vkey[j] = k;
         vvo[j] = (int)(2 * ((int64_t)k * a.vs + row));
     }
+    // Every helper lambda below is forced inline: left to the inliner, the
+    // unrolled key loop's block became a call, and the kernel's arguments
+    // went through scratch memory.
+    //
     // Queue key block [kv0, kv0 + BKV) into `stage`; with CHECK, keys past
     // seq_kv load zeros (without, the caller knows the block lies inside).
-    auto issue = [&](auto check_tag, char *stage, int kv0) {
+    auto issue = [&](auto check_tag, char *stage, int kv0) __attribute__((always_inline)) {
         constexpr bool CHECK = decltype(check_tag)::value;
 #pragma unroll
         for (int j = 0; j < K_PER; ++j) {
@@ -148,14 +177,15 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[g][db][r] = 0.0f;
     // m: the reference max of the log2-scaled scores (-inf until a key is
-    // allowed); nmu: -m, or 0 while m is -inf (the weights then stay 0);
-    // l: this lane's running sum (its half of the keys).
+    // allowed); nmu: -m, or +inf while m is -inf (which makes the next
+    // block's weights overflow and so move m); l: this lane's running sum
+    // (its half of the keys).
     float m[QG], nmu[QG], l[QG];
 #pragma unroll
-    for (int g = 0; g < QG; ++g) m[g] = -__builtin_inff(), nmu[g] = 0.0f, l[g] = 0.0f;
+    for (int g = 0; g < QG; ++g) m[g] = -__builtin_inff(), nmu[g] = __builtin_inff(), l[g] = 0.0f;
 
     // Scores of one key block: S^T = K Q^T for the wave's query groups.
-    auto qk = [&](const char *__restrict__ kt, f32x16 (&s)[QG][SB]) {
+    auto qk = [&](const char *__restrict__ kt, f32x16 (&s)[QG][SB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
 #pragma unroll
@@ -174,56 +204,49 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // Online softmax update of one key block's scores, then O^T += V^T P^T.
     // MASK: the block holds keys past seq_kv or past some query of the wave
     // (causal); interior blocks skip the per-score test.
-    auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[QG][SB], const char *__restrict__ vt, int kv0) {
+    auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[QG][SB], const char *__restrict__ vt,
+                          int kv0) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         u32x4 pf[QG][PT];
 #pragma unroll
         for (int g = 0; g < QG; ++g) {
-            // The max is taken on the raw scores (scale > 0 keeps their
-            // order); the scale folds into the exponent's fused multiply-add.
-            float mb = -__builtin_inff();
+            if constexpr (MASK) {
 #pragma unroll
-            for (int sb = 0; sb < SB; ++sb)
+                for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if constexpr (MASK) {
+                    for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + 32 * sb + 16 * (r >> 3) + 8 * half + (r & 7);
                         if (key >= a.seq_kv || (CAUSAL && key > my_q[g])) s[g][sb][r] = -__builtin_inff();
                     }
-                    mb = fmaxf(mb, s[g][sb][r]);
-                }
-            mb = scaled_max_of_halves(mb, a.scale_log2);
-            // The reference max moves only when some lane's block max exceeds
-            // it by more than 2^kAttnSlack (a wave vote); below that the
-            // weights exp2(x - m) stay under 2^kAttnSlack, and O, l and lse
-            // are relative to the same reference, so the result is the same
-            // up to rounding. With random scores the max stops growing by
-            // that much after the first blocks, so the rescaling of O is
-            // skipped from then on.
-            if (__any(mb > m[g] + kAttnSlack)) {
+            }
+            // Weights against the reference max m held so far. O, l and lse
+            // are all relative to m, so any m gives the same result up to
+            // rounding, as long as no weight overflows: their sum (every
+            // weight is >= 0) bounds each of them. Only when some lane's sum
+            // exceeds 2^8 (a wave vote; also on a query's first allowed
+            // keys, where nmu is +inf and the sum inf or NaN) does the block
+            // max move m, rescale O and l, and the weights get recomputed.
+            // With random scores that happens in the first blocks only.
+            float ps = attn_weights<TI>(s[g], pf[g], a.scale_log2, nmu[g]);
+            if (__any(!(ps <= kAttnSumLimit))) {
+                // The max is taken on the raw scores (scale > 0 keeps their order).
+                float mb = -__builtin_inff();
+#pragma unroll
+                for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s[g][sb][r]);
+                mb = scaled_max_of_halves(mb, a.scale_log2);
                 const float mn = fmaxf(m[g], mb);
-                const float nmun = mn == -__builtin_inff() ? 0.0f : -mn;
-                const float alpha = __builtin_amdgcn_exp2f(m[g] + nmun);  // 0 while m is -inf
+                const bool none = mn == -__builtin_inff();  // no key allowed yet for this query
+                const float alpha = m[g] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m[g] - mn);
                 l[g] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[g][db][r] *= alpha;
                 m[g] = mn;
-                nmu[g] = nmun;
-            }
-            float ps = -0.0f;  // -0 + p is p: the first addition folds away
-#pragma unroll
-            for (int t = 0; t < PT; ++t) {
-                uint16_t e8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][t >> 1][8 * (t & 1) + e], a.scale_log2, nmu[g]));
-                    ps += p;
-                    e8[e] = from_f32<TI>(p);
-                }
-                pf[g][t] = pack8(e8);
+                nmu[g] = none ? __builtin_inff() : -mn;
+                ps = attn_weights<TI>(s[g], pf[g], a.scale_log2, none ? 0.0f : -mn);  // no key allowed: every weight 0
             }
             l[g] += ps;
         }
@@ -240,7 +263,8 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // A whole key block; each branch of the mask test gets its own copy
     // (sharing the score products ahead of the branch raised the register
     // count from 164 to 220).
-    auto block = [&](auto mask_tag, const char *__restrict__ kt, const char *__restrict__ vt, int kv0) {
+    auto block = [&](auto mask_tag, const char *__restrict__ kt, const char *__restrict__ vt,
+                     int kv0) __attribute__((always_inline)) {
         f32x16 sc[QG][SB];
         qk(kt, sc);
         softmax_pv(mask_tag, sc, vt, kv0);
@@ -257,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     for (int s = 0; s < S - 1; ++s) issue(std::true_type{}, lds + s * STAGE, s * BKV);
     int cur = 0;
     // Block kb: wait for it, synchronise, queue block kb+S-1, then compute.
-    auto step = [&](auto mask_tag, int kb) {
+    auto step = [&](auto mask_tag, int kb) __attribute__((always_inline)) {
         wait_vmcnt<(S - 2) * LOADS>();  // block kb has landed (this wave's loads)
         stage_barrier();                // ... everyone's; and everyone is done with block kb-1
         const int fill = cur == 0 ? S - 1 : cur - 1;
@@ -284,7 +308,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // loop.
     // The block it queues lies inside seq_kv (the loop's condition), so its
     // loads skip the key test.
-    auto step_at = [&](auto u_tag, int kb) {
+    auto step_at = [&](auto u_tag, int kb) __attribute__((always_inline)) {
         constexpr int U = decltype(u_tag)::value;
         wait_vmcnt<(S - 2) * LOADS>();
         stage_barrier();

@@ -27,10 +27,10 @@ constexpr int kAttnQueryGroups = 1;  // 32-query groups per wave
 constexpr int kAttnBlockQ = 128;     // queries per workgroup (4 waves x groups x 32)
 constexpr int kAttnBlockKV = 64;     // keys per step
 constexpr int kAttnStages = 3;       // most K/V blocks in the LDS ring (head_dim 64)
-// How far (log2 units) a block's max may exceed the reference max before the
-// reference moves and O is rescaled: weights stay below 2^8, well inside the
+// The largest sum of one lane's weights in a key block that leaves the
+// reference max where it is: every weight then stays <= 2^8, well inside the
 // range of fp32 sums and of the 16-bit weights fed to the second product.
-constexpr float kAttnSlack = 8.0f;
+constexpr float kAttnSumLimit = 256.0f;
 
 // K/V blocks in the LDS ring for a head_dim: 3 x 16 KiB at 64; 2 x 32 KiB at
 // 128 (two workgroups per CU instead of one).

@@ -125,6 +125,29 @@ def test_attention_large_scores_and_custom_scale():
     check(q, k, v, "f16", "f32", True, scale=0.05, what="scale 0.05")
 
 
+def test_attention_reference_max_moves():
+    """The kernel keeps its reference max until a lane's weights in a block sum
+    past 2^8, or overflow. Head 0: scores that climb along the keys (key j
+    scaled by 0.2 + j/40, one block four times higher still), so the reference
+    moves in many blocks, by small steps and by large jumps. Head 1: every
+    score near -128 (exp2 of the log2-scaled scores, about -185, underflows
+    fp32 unless the block max is subtracted first)."""
+    B, H, Sq, Skv = 1, 2, 130, 700
+    for D in (64, 128):
+        g = torch.Generator().manual_seed(31 + D)
+        q = torch.randn(B, H, Sq, D, generator=g)
+        ramp = 0.2 + torch.arange(Skv, dtype=torch.float32) / 40.0
+        ramp[400:464] *= 4.0
+        k = torch.randn(B, H, Skv, D, generator=g) * ramp.view(1, 1, Skv, 1)
+        q[:, 1] = 4.0 + 0.05 * torch.randn(B, Sq, D, generator=g)
+        k[:, 1] = -4.0 + 0.05 * torch.randn(B, Skv, D, generator=g)
+        v = torch.randn(B, H, Skv, D, generator=g)
+        for dtype in ("bf16", "f16"):
+            for causal in (False, True):
+                check(q.to(TD[dtype]), k.to(TD[dtype]), v.to(TD[dtype]), dtype, "f32", causal,
+                      what=f"moving reference max d{D} {dtype} causal={causal}")
+
+
 def test_attention_zero_queries_average_values():
     B, H, S, D = 1, 2, 150, 64
     q = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
