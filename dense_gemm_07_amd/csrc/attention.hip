@@ -300,14 +300,11 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // of a workgroup only differ in which loop an iteration belongs to.
     const int nfree = min(nkv, (CAUSAL ? min(a.seq_kv, wq0 + 1) : a.seq_kv) / BKV);
     int kb = 0;
-    // At head_dim 64, the unmasked blocks S at a time: block kb + u lives in
-    // stage u, so every stage address is a compile-time offset and the
-    // fragment reads need no per-block address arithmetic (measured +2-3 %).
-    // At head_dim 128 the compiler moved the unrolled loop's arrays to
-    // scratch memory (704 bytes per lane, 25x slower), so it keeps the plain
-    // loop.
-    // The block it queues lies inside seq_kv (the loop's condition), so its
-    // loads skip the key test.
+    // The unmasked blocks S at a time: block kb + u lives in stage u, so
+    // every stage address is a compile-time offset and the fragment reads
+    // need no per-block address arithmetic (measured +2-3 % at head_dim 64,
+    // +4 % at 128). The block it queues lies inside seq_kv (the loop's
+    // condition), so its loads skip the key test.
     auto step_at = [&](auto u_tag, int kb) __attribute__((always_inline)) {
         constexpr int U = decltype(u_tag)::value;
         wait_vmcnt<(S - 2) * LOADS>();
@@ -316,15 +313,13 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         const int kv0 = kb * BKV;
         if (!CAUSAL || kv0 <= last_q) block(std::false_type{}, lds + U * STAGE, lds + U * STAGE + K_BYTES, kv0);
     };
-    if constexpr (D == 64) {
-        static_assert(S == 3, "the unrolled loop covers three stages");
-        for (; kb + S <= nfree && (kb + 2 * S - 1) * BKV <= a.seq_kv; kb += S) {
-            step_at(std::integral_constant<int, 0>{}, kb);
-            step_at(std::integral_constant<int, 1>{}, kb + 1);
-            step_at(std::integral_constant<int, 2>{}, kb + 2);
-        }
-        cur = kb % S;
+    static_assert(S == 2 || S == 3, "the unrolled loop covers two or three stages");
+    for (; kb + S <= nfree && (kb + 2 * S - 1) * BKV <= a.seq_kv; kb += S) {
+        step_at(std::integral_constant<int, 0>{}, kb);
+        step_at(std::integral_constant<int, 1>{}, kb + 1);
+        if constexpr (S == 3) step_at(std::integral_constant<int, 2>{}, kb + 2);
     }
+    cur = kb % S;
     for (; kb < nfree; ++kb) step(std::false_type{}, kb);
     for (; kb < nkv; ++kb) step(std::true_type{}, kb);
     wait_vmcnt<0>();  // the trailing out-of-range loads land before the workgroup exits
