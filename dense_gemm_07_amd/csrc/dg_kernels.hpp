@@ -630,12 +630,15 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &g, const EpiRows &e, co
 
 // The fused epilogue without LDS, for an interior tile whose epilogue needs
 // nothing from other lanes: no residual (beta == 0), bias absent or one per
-// column, no activation or ReLU. In the accumulator layout every register of
-// lane l in fragment column j lies in column col_base + 32j, so the lane loads
-// one bias value per fragment column and stores each element straight from its
-// register, as the plain store does (measured faster than staging the tile for
-// whole-row writes). Same arithmetic as epi_rows, absent terms as +0.
-template <typename TO, int FM, int FN>
+// column, any activation (each acts on one element). In the accumulator
+// layout every register of lane l in fragment column j lies in column
+// col_base + 32j, so the lane loads one bias value per fragment column and
+// stores each element straight from its register, as the plain store does
+// (measured faster than staging the tile for whole-row writes). Same
+// arithmetic as epi_rows, absent terms as +0. GELU is a template argument
+// (DG_ACT_GELU for fp32 outputs, kActGelu16 for 16-bit ones, as in
+// epi_rows); none and ReLU share one instantiation.
+template <typename TO, int GELU, int FM, int FN>
 __device__ __forceinline__ void epi_direct_t(const GemmArgs &g, const EpiRows &e, const f32x16 (&acc)[FM][FN],
                                              int row_base, int col_base) {
     typename TO::storage *C = reinterpret_cast<typename TO::storage *>(e.C);  // this product's C
@@ -653,18 +656,26 @@ __device__ __forceinline__ void epi_direct_t(const GemmArgs &g, const EpiRows &e
             for (int r = 0; r < 16; ++r) {
                 const int gm = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
                 float t = __builtin_fmaf(g.beta, 0.0f, g.alpha * acc[i][j][r]) + (bc[j] + 0.0f);
-                t = (relu && t < 0.0f) ? 0.0f : t;
+                if constexpr (GELU == DG_ACT_GELU) t = activate(t, DG_ACT_GELU);
+                else if constexpr (GELU == kActGelu16) t = gelu_16(t);
+                else t = (relu && t < 0.0f) ? 0.0f : t;
                 C[(int64_t)gm * g.scm + cbase] = from_f32<TO>(t);
             }
         }
 }
 
-template <int FM, int FN>
+template <int FM, int FN, bool GELU>
 __device__ __forceinline__ void epi_direct(const GemmArgs &g, const EpiRows &e, const f32x16 (&acc)[FM][FN],
                                            int row_base, int col_base) {
-    if (g.out_dtype == DG_BF16) epi_direct_t<BF16, FM, FN>(g, e, acc, row_base, col_base);
-    else if (g.out_dtype == DG_F16) epi_direct_t<F16, FM, FN>(g, e, acc, row_base, col_base);
-    else epi_direct_t<F32, FM, FN>(g, e, acc, row_base, col_base);
+    if (GELU && g.act == DG_ACT_GELU) {
+        if (g.out_dtype == DG_BF16) epi_direct_t<BF16, kActGelu16, FM, FN>(g, e, acc, row_base, col_base);
+        else if (g.out_dtype == DG_F16) epi_direct_t<F16, kActGelu16, FM, FN>(g, e, acc, row_base, col_base);
+        else epi_direct_t<F32, DG_ACT_GELU, FM, FN>(g, e, acc, row_base, col_base);
+        return;
+    }
+    if (g.out_dtype == DG_BF16) epi_direct_t<BF16, 0, FM, FN>(g, e, acc, row_base, col_base);
+    else if (g.out_dtype == DG_F16) epi_direct_t<F16, 0, FM, FN>(g, e, acc, row_base, col_base);
+    else epi_direct_t<F32, 0, FM, FN>(g, e, acc, row_base, col_base);
 }
 
 // The same tile through the fused epilogue, staged through LDS. The tile is
@@ -675,7 +686,7 @@ __device__ __forceinline__ void epi_direct(const GemmArgs &g, const EpiRows &e, 
 // requested before the staging (epi_load), and a row's 4 elements of C and of
 // the residual move as one vector when the layout allows. `st` is the
 // kernel's LDS (CAP bytes, free: the K loop is done).
-template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
+template <int BM, int BN, int WM, int WN, int FM, int FN, int CAP, bool DIRECT_GELU = true>
 __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
                                           float *st, int m0, int n0) {
     constexpr int T = WM * WN * 64;
@@ -722,8 +733,10 @@ __device__ __forceinline__ void store_epi(const GemmArgs &g, const WorkItem &w, 
     e.rvec = e.ncols == 4 && e.use_r && g.srn == 1 && g.srm % 4 == 0 &&
              ((uintptr_t)g.R + (uintptr_t)((e.r_off + e.gn0) * r_es)) % (uintptr_t)(4 * r_es) == 0;
     e.rmode = (!e.rvec || r_es == 4) ? 0 : (g.r_dtype == DG_BF16 ? 1 : 2);
-    if (!e.use_r && !e.row_bias && g.act != DG_ACT_GELU && m0 + BM <= g.M && n0 + BN <= g.N) {
-        epi_direct<FM, FN>(g, e, acc, m0 + wm * WTM + 4 * (lane >> 5), n0 + wn * WTN + (lane & 31));
+    // DIRECT_GELU false keeps GELU on the staged path (a kernel whose
+    // registers would not hold the direct path's GELU without spilling).
+    if (!e.use_r && !e.row_bias && (DIRECT_GELU || g.act != DG_ACT_GELU) && m0 + BM <= g.M && n0 + BN <= g.N) {
+        epi_direct<FM, FN, DIRECT_GELU>(g, e, acc, m0 + wm * WTM + 4 * (lane >> 5), n0 + wn * WTN + (lane & 31));
         return;
     }
     // The pass loop; the pass size is a compile-time constant, so the staging
@@ -846,11 +859,11 @@ __device__ __forceinline__ void write_tile(const GemmArgs &g, const WorkItem &w,
 }
 
 // The end of an MFMA kernel in mode EM.
-template <int EM, int BM, int BN, int WM, int WN, int FM, int FN, int CAP>
+template <int EM, int BM, int BN, int WM, int WN, int FM, int FN, int CAP, bool DIRECT_GELU = true>
 __device__ __forceinline__ void finish_tile(const GemmArgs &g, const WorkItem &w, const f32x16 (&acc)[FM][FN],
                                             float *st, int m0, int n0) {
     if constexpr (EM == EM_SPLIT) split_store<FM, FN, WM * WN * 64>(g, w, acc);  // gemm_split_reduce finishes it
-    else if constexpr (EM == EM_FUSED) store_epi<BM, BN, WM, WN, FM, FN, CAP>(g, w, acc, st, m0, n0);
+    else if constexpr (EM == EM_FUSED) store_epi<BM, BN, WM, WN, FM, FN, CAP, DIRECT_GELU>(g, w, acc, st, m0, n0);
     else write_plain<BM, BN, WM, WN, FM, FN>(g, w, acc, m0, n0);
 }
 
@@ -1907,7 +1920,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_rs(GemmArgs g) {
     if constexpr (R > 2)
         if (kt + 1 < nk) step_u(std::integral_constant<int, 1 % R>{}, kt + 1);
 
-    finish_tile<EM, BM, BN, WM, WN, FM, FN, S * STAGE>(g, w, acc, reinterpret_cast<float *>(lds), m0, n0);
+    // The 256 x 256 register-staged kernels spill with GELU in the direct
+    // epilogue (11 VGPRs), so theirs stays staged.
+    finish_tile<EM, BM, BN, WM, WN, FM, FN, S * STAGE, (BM * BN < 256 * 256)>(g, w, acc, reinterpret_cast<float *>(lds),
+                                                                          m0, n0);
 }
 
 // ============================================================================

@@ -400,8 +400,9 @@ def test_epilogue_large_tiles_bit_exact(case, cfg_shape, layouts):
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("cfg_shape", [(256, 256, 64, 2), (128, 128, 64, 2)], ids=lambda s: "x".join(map(str, s)))
 def test_epilogue_gelu_large_tiles(cfg_shape, out_dtype):
-    """GELU with a column bias on the large tiles (staged epilogue), random
-    data, within the epilogue tolerance of the oracle."""
+    """GELU with a column bias on the large tiles (interior tiles take the
+    direct epilogue, edge tiles the staged one), random data, within the
+    epilogue tolerance of the oracle."""
     case = ("bf16", out_dtype, 1.0, 0.0, None, "f32col", "gelu")
     check_epilogue(800, 800, 256, case, ("row", "row"), cfg=config("bf16", *cfg_shape), integers=False, seed=9)
 
