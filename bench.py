@@ -292,8 +292,6 @@ def main():
     ap.add_argument("--rotate", type=int, default=1, metavar="SETS",
                     help="cycle the product through SETS copies of (A, B, C), so that more than the "
                          "256 MB Infinity Cache is touched between reuses (cold-cache numbers)")
-    ap.add_argument("--vendor", action="store_true",
-                    help="also time torch.matmul (the ROCm vendor GEMM) on the same operands, for context")
     ap.add_argument("--attention", action="store_true",
                     help="time the attention forward kernel instead (--batch, --heads, --seq, --head-dim, --causal)")
     ap.add_argument("--settle-ms", type=float, default=200.0,
@@ -491,23 +489,6 @@ def main():
     if args.config or args.misalign_a:
         result["config"].update({"explicit_config": args.config, "misaligned_a": args.misalign_a})
         result["roofline"]["traffic"] = None  # the recorded counters belong to the default configuration
-    if args.vendor and not ex and nb == 1:
-        # Context only: the vendor library on the same operands and stream, same step count.
-        # torch.matmul writes the inputs' dtype; where C's dtype differs, it writes a buffer of that dtype.
-        vout = c if c.dtype == a.dtype else torch.empty(c.shape, dtype=a.dtype, device=dev)
-
-        def vstep():
-            torch.matmul(a, b, out=vout)
-        warm_up(vstep, args.warmup, args.settle_ms)
-        start.record(stream)
-        for _ in range(args.steps):
-            vstep()
-        end.record(stream)
-        torch.cuda.synchronize()
-        vms = start.elapsed_time(end) / args.steps
-        result["vendor"] = {"library": "torch.matmul (hipBLASLt)", "value": round(flops / (vms * 1e-3) / 1e12, 2),
-                            "unit": "TFLOP/s", "ms_per_step": round(vms, 5), "speedup_of_ours": round(vms / ms, 4),
-                            "out_dtype": str(vout.dtype).replace("torch.", "")}
     # Observed shader clock (the board lowers it under its power cap); the clock-adjusted
     # fraction applies to the matrix-core roof only.
     mfma = roofline["bound"] == "mfma"
