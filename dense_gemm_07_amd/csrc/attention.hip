@@ -272,8 +272,9 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
 
     // One barrier per key block. (Issuing the next block's score products
     // before this block's softmax -- a software pipeline -- needs a second
-    // score register set: 252 registers, two waves per SIMD, measured 10%
-    // slower than this loop at 164 registers and three waves per SIMD.)
+    // score register set and a deeper ring: at 190-196 registers, two waves
+    // per SIMD, with MFMA/VALU interleaving hints, it measured 1-5% slower
+    // than this loop at 156 registers and three waves per SIMD.)
     // The stage pointers never alias the stage being filled (restrict keeps
     // the compiler from waiting on those loads before reading these).
     const int last_q = wq0 + 32 * QG - 1;  // causal: blocks past it add nothing for this wave
