@@ -20,7 +20,8 @@ import torch
 import dense_gemm_07_amd as dg
 import oracle
 from dense_gemm_07_amd import inputs
-from helpers import (assert_bits_equal, assert_within_tol, epilogue_tolerance, out_bits, to_f64, ulp)
+from helpers import (assert_bits_equal, assert_within_tol, epilogue_tolerance, out_bits, sample_indices, to_f64,
+                     ulp)
 
 pytestmark = pytest.mark.gpu
 
@@ -405,6 +406,31 @@ def test_epilogue_gelu_large_tiles(cfg_shape, out_dtype):
     epilogue tolerance of the oracle."""
     case = ("bf16", out_dtype, 1.0, 0.0, None, "f32col", "gelu")
     check_epilogue(800, 800, 256, case, ("row", "row"), cfg=config("bf16", *cfg_shape), integers=False, seed=9)
+
+
+def test_mlp_bias_gelu_full_size_sampled():
+    """The fused epilogue that `bench.py --epilogue bias_gelu` times, at full
+    size: the MLP-shaped product (8192 x 14336 x 4096 bf16, its default tile
+    choice, every tile interior, so GELU runs in the register path) with an
+    fp32 bias per column, sampled entries against the oracle's product and
+    epilogue."""
+    w = inputs.WORKLOADS["mlp_8192x14336x4096_bf16"]
+    note("mlp bias + gelu, full size")
+    a_cpu, b_cpu = inputs.make(w)
+    bias = torch.randn(w.N, generator=torch.Generator().manual_seed(1))
+    c = torch.full((w.M, w.N), float("nan"), dtype=TD[w.out_dtype], device=DEV)
+    dg.gemm_ex(inputs.to_device_like(a_cpu, DEV), inputs.to_device_like(b_cpu, DEV), out=c, bias=bias.to(DEV),
+               activation="gelu")
+    torch.cuda.synchronize()
+    rows, cols = sample_indices(w.M, w.N, 3000, seed=6)
+    p = oracle.gemm_entries(inputs.bits(a_cpu, w.in_dtype), inputs.bits(b_cpu, w.in_dtype), w.in_dtype, rows, cols)
+    bb = inputs.bits(bias, "f32")[cols]
+    ref = oracle.epilogue(p.reshape(1, -1), bias_bits=bb, bias_dtype="f32", act="gelu")[0]
+    got = to_f64(c[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
+    assert np.all(np.isfinite(got)), "C not fully written"
+    terms = np.abs(p) + np.abs(bias.double().numpy()[cols])
+    assert_within_tol(got, ref, epilogue_tolerance(w.K, w.in_dtype, w.out_dtype, got, ref, 1.0, terms, "gelu"),
+                      "mlp bias + gelu")
 
 
 @pytest.mark.parametrize("case", [c for c in EPI_CASES if c[0] != "f32"], ids=lambda c: "-".join(map(str, c)))
