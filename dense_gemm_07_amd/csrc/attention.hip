@@ -98,8 +98,26 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     constexpr int PT = BKV / 16;          // k-steps of V^T P^T
     __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
-    const int bh_count = a.batch * a.heads;
-    const int qi = blockIdx.x / bh_count, bh = blockIdx.x - qi * bh_count;
+    // Workgroup order. Without a mask: the ids one XCD receives (they are
+    // dealt round-robin) get consecutive logical numbers, and consecutive
+    // numbers walk the query blocks of one (batch, head). An XCD then works
+    // on one or two heads at a time, whose workgroups read the same K/V
+    // blocks at about the same time, so its L2 serves most of them: a tenth
+    // of the fabric traffic of the head-fastest order, which put eight heads
+    // on each XCD at once (16 MiB of K/V against a 4 MiB L2 at seq 8192).
+    // Causal: head-fastest with the longest query blocks of every head
+    // first, so that the short blocks fill in at the end (walking one head
+    // at a time left each XCD's last long blocks to start late: 6 % slower).
+    int bh, qi;
+    if (CAUSAL) {
+        const int bh_count = a.batch * a.heads;
+        qi = blockIdx.x / bh_count;
+        bh = blockIdx.x - qi * bh_count;
+    } else {
+        const int lid = a.num_xcd > 1 ? xcd_rank(blockIdx.x, gridDim.x, a.num_xcd) : blockIdx.x;
+        bh = lid / a.q_blocks;
+        qi = lid - bh * a.q_blocks;
+    }
     const int qblk = CAUSAL ? a.q_blocks - 1 - qi : qi;  // causal: the longest rows start first
     const int b = bh / a.heads, h = bh - b * a.heads;
     const int tid = threadIdx.x, lane = tid & 63;

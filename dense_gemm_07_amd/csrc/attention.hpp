@@ -19,6 +19,7 @@ struct AttnArgs {
     int32_t out_dtype;  // dg_dtype of O
     int32_t q_blocks;   // query blocks per (batch, head)
     int32_t causal;
+    int32_t num_xcd;    // XCDs of the device (workgroups are dealt to them round-robin)
 };
 
 // One 32-query group per wave measured best: two groups (sharing each K/V

@@ -1067,6 +1067,7 @@ dg_status dg_attention_fwd(int64_t batch, int64_t heads, int64_t seq_q, int64_t 
     a.out_dtype = out_dtype;
     a.q_blocks = (int32_t)q_blocks;
     a.causal = causal ? 1 : 0;
+    a.num_xcd = device_info().num_xcd;
     const hipError_t err = launch_attention(a, in_dtype, (int)head_dim, (hipStream_t)stream);
     if (err != hipSuccess) return fail(DG_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
     return DG_OK;
