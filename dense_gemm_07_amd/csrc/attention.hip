@@ -105,16 +105,26 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // blocks at about the same time, so its L2 serves most of them: a tenth
     // of the fabric traffic of the head-fastest order, which put eight heads
     // on each XCD at once (16 MiB of K/V against a 4 MiB L2 at seq 8192).
-    // Causal: head-fastest with the longest query blocks of every head
-    // first, so that the short blocks fill in at the end (walking one head
-    // at a time left each XCD's last long blocks to start late: 6 % slower).
+    // Causal: the same XCD numbering, then groups of four heads whose query
+    // blocks run longest first, the group's heads interleaved, so that short
+    // blocks fill in behind long ones (walking one head at a time left each
+    // XCD's last long blocks to start late: 6 % slower; all heads at once,
+    // longest first, read twice the K/V bytes from beyond the L2).
     int bh, qi;
+    const int lid = a.num_xcd > 1 ? xcd_rank(blockIdx.x, gridDim.x, a.num_xcd) : blockIdx.x;
     if (CAUSAL) {
+        // Groups of G heads, each group's query blocks longest first with
+        // its heads interleaved: the XCD's working set is G heads' K/V, and
+        // the next group's long blocks start while this group's short ones
+        // still run.
+        constexpr int G = 4;
         const int bh_count = a.batch * a.heads;
-        qi = blockIdx.x / bh_count;
-        bh = blockIdx.x - qi * bh_count;
+        const int group = lid / (G * a.q_blocks);
+        const int gh = min(G, bh_count - group * G);  // heads in this group
+        const int r = lid - group * G * a.q_blocks;
+        qi = r / gh;
+        bh = group * G + (r - qi * gh);
     } else {
-        const int lid = a.num_xcd > 1 ? xcd_rank(blockIdx.x, gridDim.x, a.num_xcd) : blockIdx.x;
         bh = lid / a.q_blocks;
         qi = lid - bh * a.q_blocks;
     }
